@@ -1,0 +1,228 @@
+"""CPU oracle for the per-rank FSDP data path (test infrastructure only).
+
+A thin ctypes wrapper around ``fsdp_oracle.c``.  Only the test suite, the
+package smoke check and the CPU-baseline leg of ``bench.py`` may import this
+package; the library under ``sharded_fsdp_flatten_amd`` never does, and the two
+share no code.  Inputs and outputs are numpy arrays on the host.
+
+The definitions, the pages they follow and the readings taken where the pages
+are silent are stated next to each C function.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "fsdp_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
+
+
+def build(force: bool = True) -> str:
+    """Compile fsdp_oracle.c with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        lib.orc_bf16.argtypes = [ctypes.c_float]
+        lib.orc_bf16.restype = ctypes.c_uint16
+        lib.orc_bf16_array.argtypes = [_i64, _p, _p]
+        lib.orc_bf16_array.restype = None
+        lib.orc_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        lib.orc_bf16_to_f32.restype = ctypes.c_float
+        lib.orc_flat_sizes.argtypes = [_i32, _p, _i64, _p]
+        lib.orc_flat_sizes.restype = None
+        lib.orc_flat_shard.argtypes = [_i32, _p, _p, _i64, _i64, _p]
+        lib.orc_flat_shard.restype = ctypes.c_int
+        lib.orc_flat_copyout.argtypes = [_i32, _p, _p, _p]
+        lib.orc_flat_copyout.restype = None
+        lib.orc_rows_sizes.argtypes = [_i32, _p, _p, _i64, _p]
+        lib.orc_rows_sizes.restype = None
+        lib.orc_rows_shard.argtypes = [_i32, _p, _p, _p, _i64, _i64, _p]
+        lib.orc_rows_shard.restype = ctypes.c_int
+        lib.orc_rows_copyout.argtypes = [_i32, _p, _p, _i64, _p, _p]
+        lib.orc_rows_copyout.restype = None
+        lib.orc_grad_reduce.argtypes = [_i64, _i64, _p, ctypes.c_float, ctypes.c_float, _p]
+        lib.orc_grad_reduce.restype = None
+        lib.orc_adamw.argtypes = [_i64, _p, _p, _p, _p, ctypes.c_double, ctypes.c_double,
+                                  ctypes.c_double, ctypes.c_double, ctypes.c_double, _i64, _p]
+        lib.orc_adamw.restype = None
+        _lib = lib
+    return _lib
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+# --------------------------------------------------------------------------
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+def _i64_array(xs) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(list(xs), dtype=np.int64))
+
+
+def _ptr_array(arrays) -> np.ndarray:
+    return np.asarray([a.ctypes.data for a in arrays], dtype=np.uint64)
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def numel(shape: Sequence[int]) -> int:
+    n = 1
+    for d in shape:
+        n *= int(d)
+    return n
+
+
+def rows_of(shape: Sequence[int]) -> tuple[int, int]:
+    """(m, r): dim-0 length and row length; a 0-d tensor is one row of one."""
+    if len(shape) == 0:
+        return 1, 1
+    r = 1
+    for d in shape[1:]:
+        r *= int(d)
+    return int(shape[0]), r
+
+
+# --------------------------------------------------------------------------
+# public oracle API
+# --------------------------------------------------------------------------
+
+def bf16(x) -> np.ndarray:
+    """fp32 -> bf16 bit patterns (uint16), round to nearest even."""
+    x = _f32(x)
+    y = np.empty(x.shape, dtype=np.uint16)
+    _load().orc_bf16_array(x.size, _ptr(x), _ptr(y))
+    return y
+
+
+def bf16_scalar(x: float) -> int:
+    return int(_load().orc_bf16(ctypes.c_float(x)))
+
+
+def flat_sizes(numels: Sequence[int], N: int) -> tuple[int, int, int, int]:
+    """(T, S, L, pad) of a FlatParameter over N ranks."""
+    n = _i64_array(numels)
+    out = np.zeros(4, dtype=np.int64)
+    _load().orc_flat_sizes(len(n), _ptr(n), N, _ptr(out))
+    return tuple(int(v) for v in out)
+
+
+def flat_shard(params: Sequence[np.ndarray], N: int, k: int) -> np.ndarray:
+    """Rank k's FlatParameter shard (k = -1: the whole padded flat buffer)."""
+    params = [_f32(p).reshape(-1) for p in params]
+    n = _i64_array(p.size for p in params)
+    T, S, L, pad = flat_sizes(n, N)
+    out = np.empty(L if k < 0 else S, dtype=np.float32)
+    ptrs = _ptr_array(params)
+    rc = _load().orc_flat_shard(len(params), _ptr(n), _ptr(ptrs), N, k, _ptr(out))
+    if rc != 0:
+        raise MemoryError("oracle flat_shard: allocation failed")
+    return out
+
+
+def flat_copyout(shapes: Sequence[Sequence[int]], gathered: np.ndarray) -> list[np.ndarray]:
+    """Per-parameter bf16 tensors (uint16 bit patterns) from the gathered flat buffer."""
+    g = _f32(gathered).reshape(-1)
+    n = _i64_array(numel(s) for s in shapes)
+    if int(n.sum()) > g.size:
+        raise ValueError("gathered buffer shorter than the unit")
+    outs = [np.empty(tuple(s), dtype=np.uint16) for s in shapes]
+    ptrs = _ptr_array(outs)
+    _load().orc_flat_copyout(len(outs), _ptr(n), _ptr(g), _ptr(ptrs))
+    return outs
+
+
+def rows_sizes(shapes: Sequence[Sequence[int]], N: int) -> int:
+    """P_r: the per-rank segment length of an FSDP2 unit."""
+    mr = [rows_of(s) for s in shapes]
+    m = _i64_array(a for a, _ in mr)
+    r = _i64_array(b for _, b in mr)
+    out = np.zeros(1, dtype=np.int64)
+    _load().orc_rows_sizes(len(mr), _ptr(m), _ptr(r), N, _ptr(out))
+    return int(out[0])
+
+
+def rows_shard(params: Sequence[np.ndarray], N: int, k: int) -> np.ndarray:
+    """Rank k's FSDP2 segment (k = -1: all N segments, rank-major)."""
+    shapes = [p.shape for p in params]
+    flat = [_f32(p).reshape(-1) for p in params]
+    mr = [rows_of(s) for s in shapes]
+    m = _i64_array(a for a, _ in mr)
+    r = _i64_array(b for _, b in mr)
+    P_r = rows_sizes(shapes, N)
+    out = np.empty(N * P_r if k < 0 else P_r, dtype=np.float32)
+    ptrs = _ptr_array(flat)
+    _load().orc_rows_shard(len(flat), _ptr(m), _ptr(r), _ptr(ptrs), N, k, _ptr(out))
+    return out
+
+
+def rows_copyout(shapes: Sequence[Sequence[int]], N: int, gathered: np.ndarray) -> list[np.ndarray]:
+    g = _f32(gathered).reshape(-1)
+    P_r = rows_sizes(shapes, N)
+    if g.size < N * P_r:
+        raise ValueError("gathered buffer shorter than N*P_r")
+    mr = [rows_of(s) for s in shapes]
+    m = _i64_array(a for a, _ in mr)
+    r = _i64_array(b for _, b in mr)
+    outs = [np.empty(tuple(s), dtype=np.uint16) for s in shapes]
+    ptrs = _ptr_array(outs)
+    _load().orc_rows_copyout(len(outs), _ptr(m), _ptr(r), N, _ptr(g), _ptr(ptrs))
+    return outs
+
+
+def grad_reduce(contribs: Sequence[np.ndarray], pre: float = 1.0, post: float = 1.0) -> np.ndarray:
+    """fp32 reduction of N bf16 contributions (uint16 arrays of equal length)."""
+    cs = [np.ascontiguousarray(c, dtype=np.uint16).reshape(-1) for c in contribs]
+    if not cs:
+        raise ValueError("need at least one contribution")
+    length = cs[0].size
+    if any(c.size != length for c in cs):
+        raise ValueError("contributions differ in length")
+    out = np.empty(length, dtype=np.float32)
+    ptrs = _ptr_array(cs)
+    _load().orc_grad_reduce(len(cs), length, _ptr(ptrs), pre, post, _ptr(out))
+    return out
+
+
+def adamw(p: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, *, lr: float,
+          betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.0, step: int = 1,
+          want_bf16: bool = False):
+    """One AdamW step, in place on p, m, v (contiguous float32). Returns bf16(p) or None."""
+    for a in (p, g, m, v):
+        if a.dtype != np.float32 or not a.flags["C_CONTIGUOUS"]:
+            raise ValueError("adamw wants contiguous float32 arrays")
+    n = p.size
+    if not (g.size == m.size == v.size == n):
+        raise ValueError("adamw: size mismatch")
+    pb = np.empty(n, dtype=np.uint16) if want_bf16 else None
+    _load().orc_adamw(n, _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr, betas[0], betas[1], eps,
+                      weight_decay, step, _ptr(pb) if pb is not None else None)
+    return pb
