@@ -1,0 +1,224 @@
+/*
+ * fsdp_flatten.h -- C ABI of the per-rank FSDP data path on MI355X (gfx950).
+ *
+ * One rank's share of one FSDP unit: shard the unit's parameters, copy a
+ * gathered unit out into per-parameter bf16 tensors, reduce the N ranks' bf16
+ * gradient contributions for this rank's shard in fp32, and run AdamW on the
+ * shard.  Every call runs hand-written HIP kernels on the caller's stream.
+ *
+ * Sources (sections as named on each page):
+ *   [P1] "PyTorch FSDP: Experiences on Scaling Fully Sharded Data Parallel"
+ *   [P2] "FSDP Under The Hood: ZeRO-3 The PyTorch Way"
+ *   [P3] "FSDP Architecture"
+ *   [P4] "FSDP (Fully Sharded Data Parallel)"
+ *
+ * Conventions for every call
+ *   - Sizes and offsets are int64 element counts.  fp32 data is `float`; bf16
+ *     data is passed as its 16-bit pattern (`uint16_t`).
+ *   - "Device pointer" means memory the GPU can read or write (hipMalloc'd,
+ *     e.g. a torch CUDA tensor's data_ptr()).  Tables of device pointers
+ *     (`params`, `outs`, `contribs`) are HOST arrays whose entries are device
+ *     pointers; the library reads the host array during the call only.
+ *   - The caller owns every buffer.  The four data calls allocate nothing,
+ *     free nothing and do not synchronise: they enqueue kernels on `stream`
+ *     (a hipStream_t; NULL is the default stream) and return.  Buffers must
+ *     stay alive until that work has finished.
+ *   - Errors: every argument is validated on the host, before any HIP call;
+ *     a call that returns non-FSDP_OK has launched nothing and written
+ *     nothing.  FSDP_E_HIP means a launch failed (hipGetLastError).  Faults
+ *     inside kernels surface at the caller's next synchronisation, as for any
+ *     HIP work.  fsdp_last_error() returns a message for the calling thread's
+ *     last non-OK status.
+ *   - Pointer alignment is not an error: 16-byte-aligned operands take the
+ *     128-bit vector path, anything else (4-byte fp32 / 2-byte bf16 aligned)
+ *     the realigning path.  Misaligned below the element size is FSDP_E_ALIGN.
+ *   - Inputs and outputs must not overlap, except that fsdp_adam_shard updates
+ *     param, exp_avg and exp_avg_sq in place.
+ *   - A unit with no elements makes every call a no-op that returns FSDP_OK.
+ */
+#ifndef FSDP_FLATTEN_H
+#define FSDP_FLATTEN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of the ABI are the only ones the library exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define FSDP_API __attribute__((visibility("default")))
+#else
+#define FSDP_API
+#endif
+
+#define FSDP_ABI_VERSION 1
+#define FSDP_ALL_RANKS (-1)
+#define FSDP_MAX_NDIM 8
+
+typedef enum {
+    FSDP_OK = 0,
+    FSDP_E_ARG = 1,          /* null or inconsistent argument                 */
+    FSDP_E_RANGE = 2,        /* value out of its range (N, k, beta, step ...) */
+    FSDP_E_ALIGN = 3,        /* pointer not aligned to its element size       */
+    FSDP_E_OVERFLOW = 4,     /* a size overflows int64                        */
+    FSDP_E_NOMEM = 5,        /* host allocation of the unit plan failed       */
+    FSDP_E_HIP = 6,          /* a HIP runtime call or kernel launch failed    */
+    FSDP_E_UNSUPPORTED = 7   /* valid request this build does not handle      */
+} fsdp_status;
+
+/* How a unit is sharded. */
+typedef enum {
+    /* FSDP1 FlatParameter ([P1] section 3.4, "FlatParameter: Flattening,
+     * Concatenation, and Sharding", Fig. 3): the parameters are flattened
+     * row-major, concatenated in list order into T elements, right-padded
+     * with +0.0 to L = N*S where S = ceil(T/N), and rank k owns elements
+     * [k*S, (k+1)*S) ([P1] section 3.4, "Sharding Strategies").              */
+    FSDP_FLAT = 1,
+    /* FSDP2 per-parameter dim-0 sharding ([P2] section 2, "Sharding geometry";
+     * [P4] "FSDP1 vs FSDP2", torch.chunk(dim=0)): parameter i with m_i rows of
+     * r_i elements (a 0-d parameter is 1 row of 1) is cut into chunks of
+     * c_i = ceil(m_i/N) rows; rank k holds rows [min(m_i,k*c_i),
+     * min(m_i,(k+1)*c_i)).  Rank k's segment has P_r = sum_i c_i*r_i
+     * elements: the parameters in order, each zero-padded to c_i rows, so
+     * every rank sends an equal AllGather input.  A gathered buffer holds the
+     * N segments in rank order (N*P_r elements).                              */
+    FSDP_ROWS = 2
+} fsdp_layout;
+
+/* Opaque plan of one unit (the analogue of a FlatParamHandle, [P1] section
+ * 3.4): parameter shapes, offsets and sizes.  Host memory only. */
+typedef struct fsdp_unit fsdp_unit;
+
+typedef struct {
+    int32_t layout;        /* FSDP_FLAT or FSDP_ROWS                           */
+    int32_t n_params;      /* p                                                */
+    int64_t N;             /* shard count                                      */
+    int64_t T;             /* elements of the unit (sum of numel)              */
+    int64_t S;             /* elements of one rank's shard (FLAT: ceil(T/N);
+                              ROWS: P_r)                                       */
+    int64_t L;             /* N*S: elements of the gathered buffer             */
+    int64_t pad;           /* L - T                                            */
+    int64_t valid;         /* elements of rank k's shard that are real data
+                              (not padding); 0 when k == FSDP_ALL_RANKS        */
+    int64_t bytes_per_rank;/* steady-state bytes rank k keeps for this unit:
+                              fp32 param 4S + fp32 grad 4S + Adam m,v 8S
+                              ([P3] per-GPU memory breakdown, 16P/N)           */
+} fsdp_unit_sizes;
+
+/* AdamW hyper-parameters.  The scalars derived from them are computed in
+ * double on the host and rounded once to float (see fsdp_adam_shard). */
+typedef struct {
+    double lr;             /* finite                                           */
+    double beta1;          /* [0, 1)                                           */
+    double beta2;          /* [0, 1)                                           */
+    double eps;            /* finite, >= 0                                     */
+    double weight_decay;   /* finite                                           */
+    int64_t step;          /* t >= 1: the step being taken (1 for the first)   */
+} fsdp_adamw_cfg;
+
+/* Version of this header the library was built from (FSDP_ABI_VERSION). */
+FSDP_API int32_t fsdp_abi_version(void);
+
+/* Message for the calling thread's last non-OK status ("" if none).  The
+ * string stays valid until the thread's next call into the library. */
+FSDP_API const char* fsdp_last_error(void);
+
+/* Short fixed name of a status code ("FSDP_OK", "FSDP_E_ARG", ...). */
+FSDP_API const char* fsdp_status_string(int32_t status);
+
+/*
+ * Plan a unit.  n_params >= 0 parameters; parameter i has ndims[i] in
+ * [0, FSDP_MAX_NDIM] dimensions, taken in order from `dims` (so `dims` holds
+ * sum(ndims) entries, each >= 0).  N >= 1.  On success *out receives a handle
+ * that the caller frees with fsdp_unit_destroy.  Allocates host memory only;
+ * makes no HIP call.  Errors: FSDP_E_ARG (null out, or null ndims/dims with
+ * n_params > 0), FSDP_E_RANGE (layout, N, n_params, a dim or ndim out of
+ * range), FSDP_E_OVERFLOW (a size beyond int64), FSDP_E_NOMEM.
+ */
+FSDP_API fsdp_status fsdp_unit_create(int32_t layout, int32_t n_params, const int32_t* ndims,
+                             const int64_t* dims, int32_t N, fsdp_unit** out);
+
+/* Free a unit.  Work already enqueued does not use the unit (every call copies
+ * what its kernels need into their arguments), so no synchronisation is
+ * needed first.  NULL is accepted. */
+FSDP_API fsdp_status fsdp_unit_destroy(fsdp_unit* unit);
+
+/* Sizes of the unit, and of rank k's shard (k in [0,N) or FSDP_ALL_RANKS). */
+FSDP_API fsdp_status fsdp_unit_info(const fsdp_unit* unit, int32_t k, fsdp_unit_sizes* out);
+
+/* Element offset of parameter i inside the FLAT flat buffer, or inside every
+ * rank's ROWS segment (the q_i of FSDP_ROWS). */
+FSDP_API fsdp_status fsdp_unit_param_offset(const fsdp_unit* unit, int32_t i, int64_t* offset);
+
+/*
+ * Shard a unit ([P1] section 3.4, FlatParameter, Fig. 3; [P2] section 2).
+ *   params : host array of n_params device pointers, parameter i holding
+ *            numel_i contiguous fp32 elements (row-major); entries of
+ *            zero-size parameters may be NULL.
+ *   k      : rank in [0, N), or FSDP_ALL_RANKS to write every rank's shard
+ *            one after another (the gathered layout, L elements).
+ *   shard  : device pointer, S fp32 elements (L for FSDP_ALL_RANKS).
+ * FLAT writes shard[j] = F[k*S + j] with F the padded flat buffer; ROWS writes
+ * rank k's segment (its rows of every parameter, zero rows up to c_i).
+ * Results are bit-exact copies.
+ */
+FSDP_API fsdp_status fsdp_flatten_shard(const fsdp_unit* unit, const float* const* params, int32_t k,
+                               float* shard, void* stream);
+
+/*
+ * Copy a gathered unit out into per-parameter bf16 tensors with an fp32->bf16
+ * cast, round to nearest even, NaN kept NaN ([P1] section 3.4, "Native Mixed
+ * Precision and the Sharded Gradient Scaler": one full-to-low cast per
+ * FlatParameter; [P1] section 3.4, "Autograd Integration": parameters are
+ * split views of the unsharded FlatParameter; [P2] section 4, bf16 compute
+ * params).
+ *   gathered : device pointer, L fp32 elements (the N shards in rank order).
+ *              FLAT padding is never read.
+ *   outs     : host array of n_params device pointers, output i holding numel_i
+ *              bf16 elements (NULL allowed for zero-size parameters).
+ */
+FSDP_API fsdp_status fsdp_unflatten_copyout(const fsdp_unit* unit, const float* gathered,
+                                   uint16_t* const* outs, void* stream);
+
+/*
+ * Reduce the N ranks' bf16 gradient contributions for one shard in fp32
+ * ([P1] section 3.4, "Sharding Strategies" and "Communication layout": the
+ * ReduceScatter sums and rank k keeps its chunk; [P1] "Native Mixed
+ * Precision": low-precision collectives; [P2] section 3 and section 4:
+ * reduce_dtype fp32).
+ *   contribs    : host array of N device pointers; contribs[r] holds rank r's
+ *                 S bf16 gradient elements for this shard.
+ *   pre_divide  : finite, non-zero; divides every term before it is added.
+ *   post_divide : finite, non-zero; divides the sum.
+ *   grad_shard  : device pointer, S fp32 outputs.
+ * out[j] = ((c_0[j]/pre + c_1[j]/pre) + ... + c_{N-1}[j]/pre) / post, each
+ * operation one rounded binary32 operation, summed in rank order from rank 0.
+ */
+FSDP_API fsdp_status fsdp_grad_reduce_shard(const fsdp_unit* unit, const uint16_t* const* contribs,
+                                   float pre_divide, float post_divide, float* grad_shard,
+                                   void* stream);
+
+/*
+ * One AdamW step on rank-local, position-aligned shards ([P3]: parameter,
+ * gradient and both Adam moments are kept for the same positions and updated
+ * with no communication; [P1] section 3.2; [P2] appendix, torch.optim.AdamW).
+ *   param, exp_avg, exp_avg_sq : device pointers, S fp32 each, updated in place.
+ *   grad        : device pointer, S fp32.
+ *   cfg         : host pointer, read during the call.
+ *   param_bf16  : device pointer to S bf16 outputs receiving bf16(new param),
+ *                 or NULL.
+ * Scalars (double, rounded once to float): decay = 1 - lr*wd,
+ * step_size = lr/(1 - beta1^t), bc2s = sqrt(1 - beta2^t).  Per element, each
+ * a rounded binary32 operation: p = p*decay; m = beta1*m + (1-beta1)*g;
+ * v = beta2*v + (1-beta2)*(g*g); p = p - step_size*(m/(sqrt(v)/bc2s + eps)).
+ */
+FSDP_API fsdp_status fsdp_adam_shard(const fsdp_unit* unit, float* param, const float* grad,
+                            float* exp_avg, float* exp_avg_sq, const fsdp_adamw_cfg* cfg,
+                            uint16_t* param_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FSDP_FLATTEN_H */

@@ -1,0 +1,60 @@
+"""Build libfsdpflat.so (the C-ABI library) in-tree with hipcc for gfx950.
+
+    python -m sharded_fsdp_flatten_amd.build
+
+Flags that matter for results:
+  -ffp-contract=off        every float operation rounds on its own (no FMA),
+                           matching the CPU oracle's operation order;
+  -Xclang -target-feature -Xclang -packed-fp32-ops
+                           no packed-fp32 instructions are generated;
+  no -ffast-math / -fgpu-flush-denormals-to-zero: IEEE division, square root
+                           and subnormals.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_NAME = "libfsdpflat.so"
+LIB_PATH = os.path.join(HERE, LIB_NAME)
+
+SOURCES = ["kernels.hip", "plan.cpp", "fsdp_abi.cpp"]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-ffp-contract=off",
+    "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall",
+    "-Wno-unused-command-line-argument",
+    "-fvisibility=hidden",
+]
+
+
+def build(verbose: bool = False) -> str:
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC,
+           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    if proc.returncode != 0:
+        sys.stderr.write(proc.stdout)
+        raise RuntimeError("hipcc failed to build %s" % LIB_NAME)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,255 @@
+// fsdp_abi.cpp -- the C ABI declared in include/fsdp_flatten.h.
+//
+// Every entry point validates all of its arguments on the host first and only
+// then makes HIP calls, so a call that fails validation launches and writes
+// nothing (and works on a machine without a GPU).
+#include "fsdp_flatten.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "plan.h"
+
+struct fsdp_unit {
+    fsdp::UnitPlan plan;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fsdp_status fail(fsdp_status s, const std::string& msg) {
+    g_last_error = msg;
+    return s;
+}
+
+fsdp_status ok() {
+    g_last_error.clear();
+    return FSDP_OK;
+}
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+fsdp_status hip_fail(hipError_t e, const char* what) {
+    return fail(FSDP_E_HIP, std::string(what) + ": " + hipGetErrorName(e) + " (" +
+                                hipGetErrorString(e) + ")");
+}
+
+// A table of n device pointers to buffers of counts[i] elements of `elem` bytes:
+// non-null where the count is non-zero, aligned to the element size.
+fsdp_status check_ptr_table(const void* const* table, size_t n, const int64_t* counts,
+                            int64_t uniform_count, size_t elem, const char* name) {
+    bool any = false;
+    for (size_t i = 0; i < n; ++i) any = any || (counts ? counts[i] : uniform_count) > 0;
+    if (!any) return FSDP_OK;
+    if (!table) return fail(FSDP_E_ARG, std::string(name) + " table is NULL");
+    for (size_t i = 0; i < n; ++i) {
+        const int64_t c = counts ? counts[i] : uniform_count;
+        if (c == 0) continue;
+        if (!table[i])
+            return fail(FSDP_E_ARG, std::string(name) + "[" + std::to_string(i) + "] is NULL");
+        if (!aligned_to(table[i], elem))
+            return fail(FSDP_E_ALIGN, std::string(name) + "[" + std::to_string(i) +
+                                          "] is not aligned to its element size");
+    }
+    return FSDP_OK;
+}
+
+fsdp_status check_buf(const void* p, int64_t count, size_t elem, const char* name) {
+    if (count == 0) return FSDP_OK;
+    if (!p) return fail(FSDP_E_ARG, std::string(name) + " is NULL");
+    if (!aligned_to(p, elem))
+        return fail(FSDP_E_ALIGN, std::string(name) + " is not aligned to its element size");
+    return FSDP_OK;
+}
+
+std::vector<int64_t> param_numels(const fsdp::UnitPlan& u) {
+    std::vector<int64_t> n;
+    n.reserve(u.params.size());
+    for (const auto& p : u.params) n.push_back(p.numel);
+    return n;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t fsdp_abi_version(void) { return FSDP_ABI_VERSION; }
+
+const char* fsdp_last_error(void) { return g_last_error.c_str(); }
+
+const char* fsdp_status_string(int32_t s) {
+    switch (s) {
+        case FSDP_OK: return "FSDP_OK";
+        case FSDP_E_ARG: return "FSDP_E_ARG";
+        case FSDP_E_RANGE: return "FSDP_E_RANGE";
+        case FSDP_E_ALIGN: return "FSDP_E_ALIGN";
+        case FSDP_E_OVERFLOW: return "FSDP_E_OVERFLOW";
+        case FSDP_E_NOMEM: return "FSDP_E_NOMEM";
+        case FSDP_E_HIP: return "FSDP_E_HIP";
+        case FSDP_E_UNSUPPORTED: return "FSDP_E_UNSUPPORTED";
+        default: return "FSDP_E_UNKNOWN";
+    }
+}
+
+fsdp_status fsdp_unit_create(int32_t layout, int32_t n_params, const int32_t* ndims,
+                             const int64_t* dims, int32_t N, fsdp_unit** out) {
+    if (!out) return fail(FSDP_E_ARG, "out is NULL");
+    *out = nullptr;
+    fsdp_unit* u = new (std::nothrow) fsdp_unit;
+    if (!u) return fail(FSDP_E_NOMEM, "cannot allocate the unit plan");
+    std::string err;
+    int rc;
+    try {
+        rc = fsdp::plan_create(layout, n_params, ndims, dims, N, &u->plan, &err);
+    } catch (const std::bad_alloc&) {
+        delete u;
+        return fail(FSDP_E_NOMEM, "cannot allocate the unit plan");
+    }
+    if (rc != 0) {
+        delete u;
+        return fail(static_cast<fsdp_status>(rc), err);
+    }
+    *out = u;
+    return ok();
+}
+
+fsdp_status fsdp_unit_destroy(fsdp_unit* unit) {
+    delete unit;
+    return ok();
+}
+
+fsdp_status fsdp_unit_info(const fsdp_unit* unit, int32_t k, fsdp_unit_sizes* out) {
+    if (!unit || !out) return fail(FSDP_E_ARG, "unit and out must not be NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    if (k != FSDP_ALL_RANKS && (k < 0 || k >= u.N))
+        return fail(FSDP_E_RANGE, "k must be in [0, N) or FSDP_ALL_RANKS");
+    out->layout = u.layout;
+    out->n_params = static_cast<int32_t>(u.params.size());
+    out->N = u.N;
+    out->T = u.T;
+    out->S = u.S;
+    out->L = u.L;
+    out->pad = u.pad;
+    out->valid = k == FSDP_ALL_RANKS ? 0 : u.valid(k);
+    out->bytes_per_rank = 16 * u.S;
+    return ok();
+}
+
+fsdp_status fsdp_unit_param_offset(const fsdp_unit* unit, int32_t i, int64_t* offset) {
+    if (!unit || !offset) return fail(FSDP_E_ARG, "unit and offset must not be NULL");
+    if (i < 0 || static_cast<size_t>(i) >= unit->plan.params.size())
+        return fail(FSDP_E_RANGE, "parameter index out of range");
+    *offset = unit->plan.params[static_cast<size_t>(i)].offset;
+    return ok();
+}
+
+fsdp_status fsdp_flatten_shard(const fsdp_unit* unit, const float* const* params, int32_t k,
+                               float* shard, void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    if (k != FSDP_ALL_RANKS && (k < 0 || k >= u.N))
+        return fail(FSDP_E_RANGE, "k must be in [0, N) or FSDP_ALL_RANKS");
+    const int64_t out_len = k == FSDP_ALL_RANKS ? u.L : u.S;
+    const std::vector<int64_t> numels = param_numels(u);
+    fsdp_status s = check_ptr_table(reinterpret_cast<const void* const*>(params), numels.size(),
+                                    numels.data(), 0, sizeof(float), "params");
+    if (s != FSDP_OK) return s;
+    if ((s = check_buf(shard, out_len, sizeof(float), "shard")) != FSDP_OK) return s;
+    if (out_len == 0) return ok();
+    std::vector<fsdp::CopySeg> segs;
+    fsdp::plan_flatten(u, params, k, shard, &segs);
+    const hipError_t e =
+        fsdp::launch_segcopy(segs, fsdp::OutType::kF32, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_flatten_shard launch");
+    return ok();
+}
+
+fsdp_status fsdp_unflatten_copyout(const fsdp_unit* unit, const float* gathered,
+                                   uint16_t* const* outs, void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    const std::vector<int64_t> numels = param_numels(u);
+    fsdp_status s;
+    if ((s = check_buf(gathered, u.T > 0 ? u.L : 0, sizeof(float), "gathered")) != FSDP_OK)
+        return s;
+    if ((s = check_ptr_table(reinterpret_cast<const void* const*>(outs), numels.size(),
+                             numels.data(), 0, sizeof(uint16_t), "outs")) != FSDP_OK)
+        return s;
+    if (u.T == 0) return ok();
+    std::vector<fsdp::CopySeg> segs;
+    fsdp::plan_copyout(u, gathered, outs, &segs);
+    const hipError_t e =
+        fsdp::launch_segcopy(segs, fsdp::OutType::kBF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_unflatten_copyout launch");
+    return ok();
+}
+
+fsdp_status fsdp_grad_reduce_shard(const fsdp_unit* unit, const uint16_t* const* contribs,
+                                   float pre_divide, float post_divide, float* grad_shard,
+                                   void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    if (!std::isfinite(pre_divide) || pre_divide == 0.0f)
+        return fail(FSDP_E_RANGE, "pre_divide must be finite and non-zero");
+    if (!std::isfinite(post_divide) || post_divide == 0.0f)
+        return fail(FSDP_E_RANGE, "post_divide must be finite and non-zero");
+    fsdp_status s;
+    if ((s = check_ptr_table(reinterpret_cast<const void* const*>(contribs),
+                             static_cast<size_t>(u.N), nullptr, u.S, sizeof(uint16_t),
+                             "contribs")) != FSDP_OK)
+        return s;
+    if ((s = check_buf(grad_shard, u.S, sizeof(float), "grad_shard")) != FSDP_OK) return s;
+    if (u.S == 0) return ok();
+    const hipError_t e = fsdp::launch_grad_reduce(contribs, u.N, u.S, pre_divide, post_divide,
+                                                  grad_shard, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_grad_reduce_shard launch");
+    return ok();
+}
+
+fsdp_status fsdp_adam_shard(const fsdp_unit* unit, float* param, const float* grad,
+                            float* exp_avg, float* exp_avg_sq, const fsdp_adamw_cfg* cfg,
+                            uint16_t* param_bf16, void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    if (!cfg) return fail(FSDP_E_ARG, "cfg is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    if (cfg->step < 1) return fail(FSDP_E_RANGE, "step must be >= 1");
+    if (!(cfg->beta1 >= 0.0 && cfg->beta1 < 1.0)) return fail(FSDP_E_RANGE, "beta1 not in [0,1)");
+    if (!(cfg->beta2 >= 0.0 && cfg->beta2 < 1.0)) return fail(FSDP_E_RANGE, "beta2 not in [0,1)");
+    if (!std::isfinite(cfg->lr)) return fail(FSDP_E_RANGE, "lr must be finite");
+    if (!std::isfinite(cfg->eps) || cfg->eps < 0.0)
+        return fail(FSDP_E_RANGE, "eps must be finite and >= 0");
+    if (!std::isfinite(cfg->weight_decay)) return fail(FSDP_E_RANGE, "weight_decay must be finite");
+    fsdp_status s;
+    if ((s = check_buf(param, u.S, sizeof(float), "param")) != FSDP_OK) return s;
+    if ((s = check_buf(grad, u.S, sizeof(float), "grad")) != FSDP_OK) return s;
+    if ((s = check_buf(exp_avg, u.S, sizeof(float), "exp_avg")) != FSDP_OK) return s;
+    if ((s = check_buf(exp_avg_sq, u.S, sizeof(float), "exp_avg_sq")) != FSDP_OK) return s;
+    if (param_bf16 && !aligned_to(param_bf16, sizeof(uint16_t)))
+        return fail(FSDP_E_ALIGN, "param_bf16 is not aligned to its element size");
+    // Kingma & Ba's bias corrections and decoupled decay, scalars in double,
+    // each rounded once to float.
+    const double t = static_cast<double>(cfg->step);
+    fsdp::AdamScalars sc;
+    sc.decay = static_cast<float>(1.0 - cfg->lr * cfg->weight_decay);
+    sc.b1 = static_cast<float>(cfg->beta1);
+    sc.omb1 = static_cast<float>(1.0 - cfg->beta1);
+    sc.b2 = static_cast<float>(cfg->beta2);
+    sc.omb2 = static_cast<float>(1.0 - cfg->beta2);
+    sc.step_size = static_cast<float>(cfg->lr / (1.0 - std::pow(cfg->beta1, t)));
+    sc.bc2s = static_cast<float>(std::sqrt(1.0 - std::pow(cfg->beta2, t)));
+    sc.eps = static_cast<float>(cfg->eps);
+    if (u.S == 0) return ok();
+    const hipError_t e = fsdp::launch_adamw(param, grad, exp_avg, exp_avg_sq, param_bf16, u.S, sc,
+                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_adam_shard launch");
+    return ok();
+}
+
+}  // extern "C"

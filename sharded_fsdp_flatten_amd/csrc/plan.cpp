@@ -1,0 +1,282 @@
+// plan.cpp -- unit planner (host integer arithmetic only).
+#include "plan.h"
+
+#include <algorithm>
+#include <limits>
+
+namespace fsdp {
+namespace {
+
+constexpr int64_t kI64Max = std::numeric_limits<int64_t>::max();
+
+// a*b and a+b with overflow detection (operands are non-negative).
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+    if (a != 0 && b > kI64Max / a) return false;
+    *out = a * b;
+    return true;
+}
+bool add_ok(int64_t a, int64_t b, int64_t* out) {
+    if (b > kI64Max - a) return false;
+    *out = a + b;
+    return true;
+}
+int64_t ceil_div(int64_t a, int64_t b) { return a / b + (a % b != 0); }
+
+// Rows [lo, hi) of a dim-0 chunked parameter held by rank k (torch.chunk: chunks
+// of c rows; ranks past the last chunk hold none).
+void rank_rows(const ParamPlan& p, int64_t k, int64_t* lo, int64_t* hi) {
+    const int64_t c = p.chunk_rows;
+    // k*c cannot overflow: k < N and c*N <= m + N - 1 fits (checked at create).
+    *lo = std::min(p.rows, k * c);
+    *hi = std::min(p.rows, (k + 1) * c);
+}
+
+}  // namespace
+
+int64_t UnitPlan::valid(int64_t k) const {
+    if (k < 0 || k >= N) return 0;
+    if (layout == kFlat) {
+        const int64_t lo = k * S;
+        const int64_t hi = std::min(T, lo + S);
+        return hi > lo ? hi - lo : 0;
+    }
+    int64_t v = 0;
+    for (const ParamPlan& p : params) {
+        int64_t lo, hi;
+        rank_rows(p, k, &lo, &hi);
+        v += (hi - lo) * p.row_len;
+    }
+    return v;
+}
+
+int plan_create(int32_t layout, int32_t n_params, const int32_t* ndims, const int64_t* dims,
+                int32_t N, UnitPlan* out, std::string* err) {
+    // status codes match fsdp_status in include/fsdp_flatten.h
+    constexpr int kArg = 1, kRange = 2, kOverflow = 4;
+    if (layout != kFlat && layout != kRows) {
+        *err = "layout must be FSDP_FLAT (1) or FSDP_ROWS (2)";
+        return kRange;
+    }
+    if (N < 1) {
+        *err = "N (shard count) must be >= 1";
+        return kRange;
+    }
+    if (n_params < 0) {
+        *err = "n_params must be >= 0";
+        return kRange;
+    }
+    if (n_params > 0 && (!ndims || !dims)) {
+        *err = "ndims and dims must not be NULL when n_params > 0";
+        return kArg;
+    }
+    UnitPlan u;
+    u.layout = layout;
+    u.N = N;
+    u.params.resize(static_cast<size_t>(n_params));
+    int64_t d = 0;
+    for (int32_t i = 0; i < n_params; ++i) {
+        if (ndims[i] < 0 || ndims[i] > 8) {
+            *err = "parameter " + std::to_string(i) + ": ndim must be in [0, 8]";
+            return kRange;
+        }
+        ParamPlan& p = u.params[static_cast<size_t>(i)];
+        int64_t numel = 1;
+        for (int32_t a = 0; a < ndims[i]; ++a, ++d) {
+            const int64_t x = dims[d];
+            if (x < 0) {
+                *err = "parameter " + std::to_string(i) + ": negative dimension";
+                return kRange;
+            }
+            p.shape.push_back(x);
+            if (!mul_ok(numel, x, &numel)) {
+                *err = "parameter " + std::to_string(i) + ": element count overflows int64";
+                return kOverflow;
+            }
+        }
+        p.numel = numel;
+        if (ndims[i] == 0) {
+            p.rows = 1;
+            p.row_len = 1;
+        } else {
+            p.rows = p.shape[0];
+            int64_t row_len = 1;
+            for (int32_t a = 1; a < ndims[i]; ++a)
+                if (!mul_ok(row_len, p.shape[static_cast<size_t>(a)], &row_len)) {
+                    *err = "parameter " + std::to_string(i) + ": row length overflows int64";
+                    return kOverflow;
+                }
+            p.row_len = row_len;
+        }
+        if (!add_ok(u.T, numel, &u.T)) {
+            *err = "unit element count overflows int64";
+            return kOverflow;
+        }
+    }
+    if (layout == kFlat) {
+        int64_t off = 0;
+        for (ParamPlan& p : u.params) {
+            p.offset = off;
+            off += p.numel;
+        }
+        u.S = ceil_div(u.T, N);
+        if (!mul_ok(u.S, N, &u.L)) {
+            *err = "padded unit length overflows int64";
+            return kOverflow;
+        }
+    } else {
+        int64_t q = 0;
+        for (ParamPlan& p : u.params) {
+            p.chunk_rows = ceil_div(p.rows, N);
+            int64_t seg, tmp;
+            if (!mul_ok(p.chunk_rows, p.row_len, &seg) || !mul_ok(p.chunk_rows, N, &tmp)) {
+                *err = "rank segment size overflows int64";
+                return kOverflow;
+            }
+            p.offset = q;
+            if (!add_ok(q, seg, &q)) {
+                *err = "rank segment size overflows int64";
+                return kOverflow;
+            }
+        }
+        u.S = q;
+        if (!mul_ok(u.S, N, &u.L)) {
+            *err = "gathered length overflows int64";
+            return kOverflow;
+        }
+    }
+    u.pad = u.L - u.T;
+    int64_t bytes;  // the 16*S per-rank ledger must be representable
+    if (!mul_ok(u.S, 16, &bytes)) {
+        *err = "per-rank byte count overflows int64";
+        return kOverflow;
+    }
+    *out = std::move(u);
+    return 0;
+}
+
+void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, float* out,
+                  std::vector<CopySeg>* segs) {
+    segs->clear();
+    if (u.layout == kFlat) {
+        const int64_t base = k < 0 ? 0 : k * u.S;
+        const int64_t len = k < 0 ? u.L : u.S;
+        for (size_t i = 0; i < u.params.size(); ++i) {
+            const ParamPlan& p = u.params[i];
+            const int64_t lo = std::max(p.offset, base);
+            const int64_t hi = std::min(p.offset + p.numel, base + len);
+            if (lo >= hi) continue;
+            CopySeg s;
+            s.src = params[i] + (lo - p.offset);
+            s.dst = out + (lo - base);
+            s.blk_n = s.last_n = hi - lo;
+            s.nblk = 1;
+            segs->push_back(s);
+        }
+        const int64_t zlo = std::max(u.T, base);
+        if (zlo < base + len) {
+            CopySeg s;
+            s.dst = out + (zlo - base);
+            s.blk_n = s.last_n = base + len - zlo;
+            s.nblk = 1;
+            segs->push_back(s);
+        }
+        return;
+    }
+    // ROWS: ranks [k0, k1) write one after another, rank segment of S elements each.
+    const int64_t k0 = k < 0 ? 0 : k;
+    const int64_t k1 = k < 0 ? u.N : k + 1;
+    for (size_t i = 0; i < u.params.size(); ++i) {
+        const ParamPlan& p = u.params[i];
+        const int64_t c = p.chunk_rows, r = p.row_len;
+        const int64_t seg_n = c * r;
+        if (seg_n == 0) continue;
+        // ranks whose chunk is complete (c rows), the one short rank, then empty ranks
+        const int64_t n_full = p.rows / c;
+        const int64_t short_rows = p.rows - n_full * c;
+        float* base = out + p.offset;
+        {  // full ranks in [k0, k1)
+            const int64_t a = k0, b = std::min(k1, n_full);
+            if (a < b) {
+                CopySeg s;
+                s.src = params[i] + a * seg_n;
+                s.dst = base + (a - k0) * u.S;
+                s.blk_n = s.last_n = seg_n;
+                s.src_stride = seg_n;
+                s.dst_stride = u.S;
+                s.nblk = b - a;
+                segs->push_back(s);
+            }
+        }
+        int64_t first_empty = n_full;
+        if (short_rows > 0) {
+            first_empty = n_full + 1;
+            const int64_t ks = n_full;
+            if (ks >= k0 && ks < k1) {
+                CopySeg s;
+                s.src = params[i] + ks * seg_n;
+                s.dst = base + (ks - k0) * u.S;
+                s.blk_n = s.last_n = short_rows * r;
+                s.nblk = 1;
+                segs->push_back(s);
+                CopySeg z;
+                z.dst = base + (ks - k0) * u.S + short_rows * r;
+                z.blk_n = z.last_n = (c - short_rows) * r;
+                z.nblk = 1;
+                segs->push_back(z);
+            }
+        }
+        {  // empty ranks: c zero rows each
+            const int64_t a = std::max(k0, first_empty), b = k1;
+            if (a < b) {
+                CopySeg z;
+                z.dst = base + (a - k0) * u.S;
+                z.blk_n = z.last_n = seg_n;
+                z.dst_stride = u.S;
+                z.nblk = b - a;
+                segs->push_back(z);
+            }
+        }
+    }
+}
+
+void plan_copyout(const UnitPlan& u, const float* gathered, uint16_t* const* outs,
+                  std::vector<CopySeg>* segs) {
+    segs->clear();
+    for (size_t i = 0; i < u.params.size(); ++i) {
+        const ParamPlan& p = u.params[i];
+        if (p.numel == 0) continue;
+        if (u.layout == kFlat) {
+            CopySeg s;
+            s.src = gathered + p.offset;
+            s.dst = outs[i];
+            s.blk_n = s.last_n = p.numel;
+            s.nblk = 1;
+            segs->push_back(s);
+            continue;
+        }
+        const int64_t c = p.chunk_rows, r = p.row_len;
+        const int64_t seg_n = c * r;
+        const int64_t n_full = p.rows / c;
+        const int64_t short_rows = p.rows - n_full * c;
+        if (n_full > 0) {
+            CopySeg s;
+            s.src = gathered + p.offset;
+            s.dst = outs[i];
+            s.blk_n = s.last_n = seg_n;
+            s.src_stride = u.S;
+            s.dst_stride = seg_n;
+            s.nblk = n_full;
+            segs->push_back(s);
+        }
+        if (short_rows > 0) {
+            CopySeg s;
+            s.src = gathered + n_full * u.S + p.offset;
+            s.dst = outs[i] + n_full * seg_n;
+            s.blk_n = s.last_n = short_rows * r;
+            s.nblk = 1;
+            segs->push_back(s);
+        }
+    }
+}
+
+}  // namespace fsdp

@@ -1,0 +1,68 @@
+// plan.h -- host-side unit planner: sizes, offsets and the copy segments that the
+// data-movement kernels execute.  Pure integer arithmetic; no HIP.
+//
+// Layouts follow "PyTorch FSDP: Experiences on Scaling Fully Sharded Data
+// Parallel" section 3.4 ("FlatParameter: Flattening, Concatenation, and
+// Sharding", Fig. 3) for FSDP1 and "FSDP Under The Hood: ZeRO-3 The PyTorch Way"
+// section 2 ("Sharding geometry") with torch.chunk(dim=0) semantics for FSDP2.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace fsdp {
+
+enum Layout : int32_t { kFlat = 1, kRows = 2 };
+
+struct ParamPlan {
+    std::vector<int64_t> shape;
+    int64_t numel = 0;
+    int64_t rows = 0;        // m: length of dim 0 (1 for a 0-d parameter)
+    int64_t row_len = 0;     // r: elements per row (product of trailing dims)
+    int64_t chunk_rows = 0;  // c = ceil(m/N) (FSDP2)
+    int64_t offset = 0;      // FLAT: first flat index; ROWS: offset q_i inside a rank segment
+};
+
+struct UnitPlan {
+    int32_t layout = kFlat;
+    int64_t N = 1;
+    int64_t T = 0;    // elements of the unit
+    int64_t S = 0;    // elements of one rank's shard (FLAT ceil(T/N), ROWS P_r)
+    int64_t L = 0;    // N*S
+    int64_t pad = 0;  // L - T
+    std::vector<ParamPlan> params;
+
+    // Real (non-padding) elements of rank k's shard.
+    int64_t valid(int64_t k) const;
+};
+
+// Builds the plan; returns 0 or an fsdp_status code with *err set.
+int plan_create(int32_t layout, int32_t n_params, const int32_t* ndims, const int64_t* dims,
+                int32_t N, UnitPlan* out, std::string* err);
+
+// One planned movement: `nblk` blocks; block b moves `blk_n` elements (the last
+// block `last_n`) from src + b*src_stride to dst + b*dst_stride.  src == nullptr
+// means "write zeros".  Strides and counts are in elements of the respective
+// buffer (fp32 for src; fp32 or bf16 for dst).
+struct CopySeg {
+    const float* src = nullptr;
+    void* dst = nullptr;
+    int64_t blk_n = 0;
+    int64_t last_n = 0;
+    int64_t src_stride = 0;
+    int64_t dst_stride = 0;
+    int64_t nblk = 0;
+};
+
+// Segments that write rank k's shard (k = -1: every rank, gathered layout) into
+// `out` from the parameters.
+void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, float* out,
+                  std::vector<CopySeg>* segs);
+
+// Segments that copy the gathered buffer out into per-parameter tensors
+// (dst elements are bf16).
+void plan_copyout(const UnitPlan& u, const float* gathered, uint16_t* const* outs,
+                  std::vector<CopySeg>* segs);
+
+}  // namespace fsdp

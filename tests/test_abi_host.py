@@ -1,0 +1,286 @@
+"""Host-side checks of the C-ABI library: it loads, exports what the header declares,
+plans units exactly as the oracle lays them out, keeps the pages' memory ledger,
+and rejects every invalid argument before making any HIP call (so all of this
+runs without a GPU)."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import workloads as W
+from conftest import ROOT, golden_path
+
+HEADER = os.path.join(ROOT, "include", "fsdp_flatten.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from sharded_fsdp_flatten_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from sharded_fsdp_flatten_amd import build
+        build.build()
+    binding.load()
+    return binding
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"FSDP_API\s+[\w\s\*]+?\b(fsdp_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("fsdp_flatten_shard", "fsdp_unflatten_copyout", "fsdp_grad_reduce_shard",
+              "fsdp_adam_shard"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    lib = B.load()
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing
+    assert sorted(_declared()) == sorted(B.ABI_FUNCTIONS)
+
+
+def test_abi_version_matches_header(B):
+    v = int(re.search(r"#define FSDP_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert B.fsdp_abi_version() == v
+
+
+def _labelled(shapes):
+    out = []
+    for s in shapes:
+        n = int(np.prod(s, dtype=np.int64)) if len(s) else 1
+        out.append(np.ones(n, np.float32).reshape(s))
+    return out
+
+
+@pytest.mark.parametrize("layout", [W.FLAT, W.ROWS])
+def test_planner_sizes_match_oracle(B, orc, layout):
+    """T, S, L, pad, per-rank valid counts and offsets agree with the oracle's own
+    layout (valid counts read off the oracle by counting the non-zero elements of a
+    shard of all-ones parameters)."""
+    rng = np.random.Generator(np.random.PCG64(31))
+    for trial in range(80):
+        shapes = W.random_unit_shapes(rng, max_params=5, max_dim=6)
+        params = _labelled(shapes)
+        for N in (1, 2, 3, 5, 8):
+            u = B.fsdp_unit_create(layout, shapes, N)
+            info = u.info()
+            T = sum(p.size for p in params)
+            if layout == W.FLAT:
+                T2, S, L, pad = orc.flat_sizes([p.size for p in params], N)
+                assert (info["T"], info["S"], info["L"], info["pad"]) == (T2, S, L, pad)
+                off = 0
+                for i, p in enumerate(params):
+                    assert u.offset(i) == off
+                    off += p.size
+            else:
+                P_r = orc.rows_sizes(shapes, N)
+                assert (info["T"], info["S"], info["L"]) == (T, P_r, N * P_r)
+                assert info["pad"] == N * P_r - T
+            for k in range(N):
+                shard = (orc.flat_shard(params, N, k) if layout == W.FLAT
+                         else orc.rows_shard(params, N, k))
+                ik = u.info(k)
+                assert ik["valid"] == int(np.count_nonzero(shard)), (shapes, N, k)
+                assert ik["bytes_per_rank"] == 16 * ik["S"]
+
+
+def _ledger():
+    vals = {}
+    with open(golden_path("memory_ledger.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                key, val, unit, dec = [x.strip() for x in line.split("|")]
+                vals[key] = (float(val), unit, int(dec))
+    return vals
+
+
+def _gpt2_large_units():
+    """GPT-2 Large as the page's script wraps it: one unit per transformer block plus
+    the root unit with the embeddings and the final LayerNorm."""
+    _, block = W.gpt_block(1280)
+    root = [(50257, 1280), (1024, 1280), (1280,), (1280,)]
+    return [block] * 36 + [root]
+
+
+def test_memory_ledger_matches_pages(B):
+    """"FSDP Architecture" per-GPU ledger 4P/N + 4P/N + 8P/N with its 13B example, and the
+    GPT-2 Large figures of "FSDP Under The Hood" section 5 (Psi = 0.774B)."""
+    L = _ledger()
+    GB, GiB = 1e9, 2.0 ** 30
+
+    def same(key, x):
+        val, unit, dec = L[key]
+        scale = {"GB": GB, "GiB": GiB, "G": 1e9}[unit]
+        assert round(x / scale, dec) == val, (key, x / scale)
+
+    u13 = B.fsdp_unit_create(B.FSDP_FLAT, [(13_000_000_000,)], 8)
+    same("p3_13b_per_gpu_n8", u13.info(0)["bytes_per_rank"])
+    same("p3_13b_total", B.fsdp_unit_create(B.FSDP_FLAT, [(13_000_000_000,)], 1).info(0)["bytes_per_rank"])
+
+    units = _gpt2_large_units()
+    psi = sum(B.fsdp_unit_create(B.FSDP_ROWS, shapes, 1).info()["T"] for shapes in units)
+    assert psi == 774_030_080
+    same("p2_psi", psi)
+    same("p2_ddp_16psi", sum(B.fsdp_unit_create(B.FSDP_FLAT, s, 1).info(0)["bytes_per_rank"]
+                             for s in units))
+    fsdp2 = sum(12 * B.fsdp_unit_create(B.FSDP_ROWS, s, 8).info(0)["S"] for s in units)
+    same("p2_fsdp2_12psi_over_8", fsdp2)
+    same("p2_bf16_model", 2 * psi)
+    same("p2_bf16_model_gb", 2 * psi)
+    same("p2_fp32_grads", 4 * psi)
+
+
+# ---------------------------------------------------------------------------
+# validation: every error is reported before any HIP call
+# ---------------------------------------------------------------------------
+
+FAKE = 0x7F0000000000  # 256-byte aligned address that is never dereferenced
+
+
+def _status(exc):
+    return exc.value.status_name
+
+
+def test_create_errors(B):
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unit_create(3, [(4,)], 2)
+    assert _status(e) == "FSDP_E_RANGE"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unit_create(B.FSDP_FLAT, [(4,)], 0)
+    assert _status(e) == "FSDP_E_RANGE"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unit_create(B.FSDP_FLAT, [(4, -1)], 2)
+    assert _status(e) == "FSDP_E_RANGE"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unit_create(B.FSDP_FLAT, [(1,) * 9], 2)
+    assert _status(e) == "FSDP_E_RANGE"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unit_create(B.FSDP_FLAT, [(2 ** 40, 2 ** 40)], 2)
+    assert _status(e) == "FSDP_E_OVERFLOW"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unit_create(B.FSDP_FLAT, [(2 ** 62,), (2 ** 62,)], 2)
+    assert _status(e) == "FSDP_E_OVERFLOW"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unit_create(B.FSDP_ROWS, [(2 ** 62, 3)], 2)
+    assert _status(e) == "FSDP_E_OVERFLOW"
+    assert "overflow" in B.fsdp_last_error()
+    lib = B.load()
+    assert lib.fsdp_unit_create(1, 0, None, None, 1, None) == 1  # null out
+    import ctypes
+    out = ctypes.c_void_p()
+    assert lib.fsdp_unit_create(1, 2, None, None, 1, ctypes.byref(out)) == 1  # null tables
+
+
+def test_info_and_offset_errors(B):
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(4,), (3,)], 2)
+    for k in (2, -2, 100):
+        with pytest.raises(B.FsdpError) as e:
+            u.info(k)
+        assert _status(e) == "FSDP_E_RANGE"
+    with pytest.raises(B.FsdpError):
+        u.offset(2)
+
+
+def test_flatten_errors(B):
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(4,), (3,)], 2)
+    cases = [
+        (dict(params=[FAKE, FAKE], k=2, shard=FAKE), "FSDP_E_RANGE"),
+        (dict(params=[FAKE, FAKE], k=-2, shard=FAKE), "FSDP_E_RANGE"),
+        (dict(params=[FAKE, 0], k=0, shard=FAKE), "FSDP_E_ARG"),
+        (dict(params=[FAKE + 2, FAKE], k=0, shard=FAKE), "FSDP_E_ALIGN"),
+        (dict(params=[FAKE, FAKE], k=0, shard=0), "FSDP_E_ARG"),
+        (dict(params=[FAKE, FAKE], k=0, shard=FAKE + 1), "FSDP_E_ALIGN"),
+    ]
+    for kw, want in cases:
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_flatten_shard(u, kw["params"], kw["k"], kw["shard"], stream=0)
+        assert _status(e) == want, kw
+    lib = B.load()
+    assert lib.fsdp_flatten_shard(u.handle, None, 0, FAKE, None) == 1  # null table
+
+
+def test_copyout_errors(B):
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(4,), (3,)], 2)
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unflatten_copyout(u, 0, [FAKE, FAKE], stream=0)
+    assert _status(e) == "FSDP_E_ARG"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unflatten_copyout(u, FAKE, [FAKE, FAKE + 1], stream=0)
+    assert _status(e) == "FSDP_E_ALIGN"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_unflatten_copyout(u, FAKE + 2, [FAKE, FAKE], stream=0)
+    assert _status(e) == "FSDP_E_ALIGN"
+
+
+def test_reduce_errors(B):
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(16,)], 4)
+    good = [FAKE] * 4
+    for pre, post in [(0.0, 1.0), (1.0, 0.0), (float("inf"), 1.0), (1.0, float("nan")),
+                      (float("nan"), 1.0), (-0.0, 1.0)]:
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_grad_reduce_shard(u, good, pre, post, FAKE, stream=0)
+        assert _status(e) == "FSDP_E_RANGE"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_grad_reduce_shard(u, [FAKE, 0, FAKE, FAKE], 1.0, 1.0, FAKE, stream=0)
+    assert _status(e) == "FSDP_E_ARG"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_grad_reduce_shard(u, [FAKE, FAKE + 1, FAKE, FAKE], 1.0, 1.0, FAKE, stream=0)
+    assert _status(e) == "FSDP_E_ALIGN"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_grad_reduce_shard(u, good, 1.0, 1.0, FAKE + 2, stream=0)
+    assert _status(e) == "FSDP_E_ALIGN"
+    with pytest.raises(ValueError):
+        B.fsdp_grad_reduce_shard(u, good[:3], 1.0, 1.0, FAKE, stream=0)
+
+
+def test_adam_errors(B):
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(16,)], 4)
+    base = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01, step=1)
+    bad = [dict(step=0), dict(step=-3), dict(betas=(1.0, 0.999)), dict(betas=(0.9, -0.1)),
+           dict(betas=(float("nan"), 0.9)), dict(eps=-1.0), dict(eps=float("inf")),
+           dict(lr=float("nan")), dict(weight_decay=float("inf"))]
+    for b in bad:
+        kw = dict(base, **b)
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_adam_shard(u, FAKE, FAKE, FAKE, FAKE, stream=0, **kw)
+        assert _status(e) == "FSDP_E_RANGE", b
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_adam_shard(u, 0, FAKE, FAKE, FAKE, stream=0, **base)
+    assert _status(e) == "FSDP_E_ARG"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_adam_shard(u, FAKE, FAKE, FAKE + 2, FAKE, stream=0, **base)
+    assert _status(e) == "FSDP_E_ALIGN"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_adam_shard(u, FAKE, FAKE, FAKE, FAKE, param_bf16=FAKE + 1, stream=0, **base)
+    assert _status(e) == "FSDP_E_ALIGN"
+    lib = B.load()
+    assert lib.fsdp_adam_shard(u.handle, FAKE, FAKE, FAKE, FAKE, None, None, None) == 1
+
+
+def test_empty_unit_calls_are_noops(B):
+    """A unit with no elements: every call validates and returns OK without launching."""
+    for layout in (B.FSDP_FLAT, B.FSDP_ROWS):
+        for shapes in ([], [(0,)], [(0, 5), (3, 0)]):
+            u = B.fsdp_unit_create(layout, shapes, 4)
+            assert u.info()["T"] == 0
+            B.fsdp_flatten_shard(u, [0] * len(shapes), 0, 0, stream=0)
+            B.fsdp_flatten_shard(u, [0] * len(shapes), B.FSDP_ALL_RANKS, 0, stream=0)
+            B.fsdp_unflatten_copyout(u, 0, [0] * len(shapes), stream=0)
+            B.fsdp_grad_reduce_shard(u, [0] * 4, 1.0, 1.0, 0, stream=0)
+            B.fsdp_adam_shard(u, 0, 0, 0, 0, lr=1e-3, stream=0)
+            assert B.fsdp_last_error() == ""
+
+
+def test_last_error_is_per_call(B):
+    with pytest.raises(B.FsdpError):
+        B.fsdp_unit_create(B.FSDP_FLAT, [(4,)], 0)
+    assert B.fsdp_last_error() != ""
+    B.fsdp_unit_create(B.FSDP_FLAT, [(4,)], 1)
+    assert B.fsdp_last_error() == ""
+    assert B.fsdp_status_string(3) == "FSDP_E_ALIGN"
+    assert B.fsdp_status_string(99) == "FSDP_E_UNKNOWN"
