@@ -1,0 +1,321 @@
+#!/usr/bin/env python3
+"""Benchmark of the per-rank FSDP data path on one MI355X.
+
+One step is one pass of the whole hot path for one rank's share of one FSDP unit:
+  grad reduce  (N bf16 gradient contributions -> fp32 shard, pre/post divide)
+  copy-out     (gathered fp32 unit -> per-parameter bf16 tensors)
+  AdamW        (param/grad/m/v shard, in place)
+  flatten      (the unit's fp32 parameters -> this rank's shard)
+The four run in that order so that every kernel reads data last touched at least
+10 GB of traffic earlier: no input can still sit in the 256 MB Infinity Cache,
+and every byte counted comes from HBM.  Inputs are synthetic (seeded normals in
+the unit's shapes) and already resident in HBM when the timed region starts.
+
+Default workload: GPT-175B style block unit (d = 12288, 1,812,099,072 fp32
+elements), FSDP1 flat sharding over N = 128, rank 63.
+
+Prints one JSON line (metric, value in GB/s over the whole step, per-kernel
+GB/s, fraction of the 8 TB/s HBM peak and elements/s, the roofline of the
+dominant kernel, and the CPU oracle timed on a bounded sample as a baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "achieved HBM GB/s (% of peak) + elements/s per kernel, one FSDP unit"
+KERNEL_SRC = os.path.join(ROOT, "sharded_fsdp_flatten_amd", "csrc", "kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gpt175b_block.json")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="gpt175b",
+                    choices=["gpt175b", "t5", "gpt2l", "rows", "tiny"])
+    ap.add_argument("--rank", type=int, default=None, help="rank k (default: N/2 - 1)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--contribs", default="stacked", choices=["stacked", "separate"],
+                    help="gradient contributions as one [N, S] receive buffer (default) or as "
+                         "N separate allocations")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also time a plain 4 GiB fp32 copy through the library (N = 1 unit) "
+                         "and hipMemcpy device-to-device, as copy ceilings")
+    return ap.parse_args()
+
+
+def kernel_src_hash() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def load_traffic(per_launch_bytes_expected):
+    """HBM bytes per copy-out launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_src_sha256") != kernel_src_hash():
+        return None
+    return t.get("copyout_hbm_bytes_per_launch")
+
+
+def make_unit(name):
+    import workloads as W
+    return {"gpt175b": W.gpt175b_block, "t5": W.t5_11b_block, "gpt2l": W.gpt2_large_block,
+            "rows": W.gpt2_large_emb_rows, "tiny": W.tiny_mlp}[name]()
+
+
+def pre_post(N):
+    """Mean over N ranks split into a pre and a post divide (powers of two when N is)."""
+    pre = 1.0
+    while pre * pre * 4 <= N:
+        pre *= 2.0
+    return pre, N / pre
+
+
+def cpu_baseline(host, unit, N, k, S, valid, pre, post, hp, rows):
+    """The CPU oracle, as it stands, on a bounded sample of the same workload:
+    flatten of rank k (whole, it builds the full flat buffer first), copy-out of the whole
+    unit, the reduction over the first S/8 outputs of the shard (all N ranks), and AdamW
+    on the whole shard.  Single thread."""
+    import numpy as np
+    import oracle
+
+    t_tot, b_tot, parts = 0.0, 0.0, {}
+
+    t0 = time.perf_counter()
+    if rows:
+        oracle.rows_shard(host["params"], N, k)
+    else:
+        oracle.flat_shard(host["params"], N, k)
+    dt = time.perf_counter() - t0
+    parts["flatten"] = (4 * valid + 4 * S, dt)
+
+    t0 = time.perf_counter()
+    if rows:
+        oracle.rows_copyout(unit.shapes, N, host["gathered"])
+    else:
+        oracle.flat_copyout(unit.shapes, host["gathered"])
+    dt = time.perf_counter() - t0
+    parts["copyout"] = (6 * unit.total, dt)
+
+    n_red = S // 8
+    cs = [np.ascontiguousarray(host["contribs"][r, :n_red]) for r in range(N)]
+    t0 = time.perf_counter()
+    g = oracle.grad_reduce(cs, pre, post)
+    dt = time.perf_counter() - t0
+    parts["grad_reduce"] = ((2 * N + 4) * n_red, dt)
+
+    p = host["adam_p"].copy()
+    gg = host["adam_g"]
+    m = np.zeros(S, np.float32)
+    v = np.zeros(S, np.float32)
+    t0 = time.perf_counter()
+    oracle.adamw(p, gg, m, v, step=1, **hp)
+    dt = time.perf_counter() - t0
+    parts["adamw"] = (28 * S, dt)
+
+    for b, dt in parts.values():
+        b_tot += b
+        t_tot += dt
+    return {
+        "value": round(b_tot / t_tot / 1e9, 3),
+        "unit": "GB/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": ("%s unit, N=%d, rank %d: flatten of the rank (whole), copy-out of the whole "
+                   "unit, reduction of the first S/8=%d outputs over all %d ranks, AdamW on the "
+                   "whole shard; single-threaded C oracle" % (unit.name, N, k, n_red, N)),
+        "per_kernel_gbs": {name: round(b / dt / 1e9, 3) for name, (b, dt) in parts.items()},
+        "seconds": round(t_tot, 2),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one rank's share of one FSDP unit on ONE GPU; --gpus %d is not "
+              "supported (no collectives are part of this build)" % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as W
+    from sharded_fsdp_flatten_amd import binding as B
+
+    if not os.path.exists(B.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    B.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    unit = make_unit(args.workload)
+    N = unit.N
+    k = args.rank if args.rank is not None else max(0, N // 2 - 1)
+    layout = B.FSDP_FLAT if unit.layout == W.FLAT else B.FSDP_ROWS
+    u = B.fsdp_unit_create(layout, unit.shapes, N)
+    info = u.info(k)
+    S, L, T, valid = info["S"], info["L"], info["T"], info["valid"]
+    pre, post = pre_post(N)
+    hp = dict(unit.adam)
+
+    # ---- inputs, resident in HBM before the timed region -------------------------
+    params = W.device_params(unit, seed=0)
+    gen = torch.Generator(device=dev).manual_seed(12345)
+    gathered = torch.randn(L, device=dev, generator=gen).mul_(unit.std)
+    outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in unit.shapes]
+    contribs = W.device_contribs(N, S, step=1)
+    if args.contribs == "stacked":
+        contrib_rows = [contribs[r] for r in range(N)]
+    else:
+        contrib_rows = [contribs[r].clone() for r in range(N)]
+    grad = torch.zeros(S, device=dev)  # written by the reduction, read by AdamW
+    shard = torch.empty(S, device=dev)
+    adam_p = torch.empty(S, device=dev)
+    B.fsdp_flatten_shard(u, params, k, adam_p)
+    m = torch.zeros(S, device=dev)
+    v = torch.zeros(S, device=dev)
+    torch.cuda.synchronize()
+
+    bytes_k = {
+        "grad_reduce": (2 * N + 4) * S,
+        "copyout": 6 * T,
+        "adamw": 28 * S,
+        "flatten": 4 * valid + 4 * S,
+    }
+    elems_k = {"grad_reduce": S, "copyout": T, "adamw": S, "flatten": S}
+    order = ["grad_reduce", "copyout", "adamw", "flatten"]
+    stream = torch.cuda.current_stream()
+    step_no = [0]
+
+    def run(name):
+        if name == "grad_reduce":
+            B.fsdp_grad_reduce_shard(u, contrib_rows, pre, post, grad)
+        elif name == "copyout":
+            B.fsdp_unflatten_copyout(u, gathered, outs)
+        elif name == "adamw":
+            step_no[0] += 1
+            B.fsdp_adam_shard(u, adam_p, grad, m, v, step=step_no[0], **hp)
+        else:
+            B.fsdp_flatten_shard(u, params, k, shard)
+
+    def step(events=None):
+        for name in order:
+            if events is not None:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run(name)
+                e1.record(stream)
+                events[name].append((e0, e1))
+            else:
+                run(name)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = {n: [] for n in order}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms_k = {n: sum(a.elapsed_time(b) for a, b in events[n]) / args.steps for n in order}
+    ms_step = wall * 1e3 / args.steps
+    step_bytes = sum(bytes_k.values())
+    kernels = {}
+    for n in order:
+        gbs = bytes_k[n] / (ms_k[n] * 1e-3) / 1e9
+        kernels[n] = {"ms": round(ms_k[n], 4), "bytes": bytes_k[n], "GB/s": round(gbs, 1),
+                      "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                      "elements_per_s": float("%.4g" % (elems_k[n] / (ms_k[n] * 1e-3)))}
+    kernels["grad_reduce"]["input_elements_per_s"] = float(
+        "%.4g" % (N * S / (ms_k["grad_reduce"] * 1e-3)))
+
+    dom = max(order, key=lambda n: ms_k[n])
+    achieved = bytes_k[dom] / (ms_k[dom] * 1e-3) / 1e9
+    traffic = load_traffic(bytes_k["copyout"]) if dom == "copyout" else None
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "%s unit (%d params, T=%d fp32 elements), %s sharding over "
+                               "N=%d, rank %d" % (unit.name, len(unit.shapes), T,
+                                                  "FSDP1 flat" if layout == B.FSDP_FLAT
+                                                  else "FSDP2 dim-0 row", N, k),
+                   "N": N, "rank": k, "S": S, "T": T, "pre_divide": pre, "post_divide": post,
+                   "contribs": args.contribs},
+        "kernels": kernels,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+    }
+
+    if args.copy_probe:
+        n = 1 << 30
+        a = torch.randn(n, device=dev, generator=gen)
+        b = torch.empty(n, device=dev)
+        cu = B.fsdp_unit_create(B.FSDP_FLAT, [(n,)], 1)
+        for _ in range(3):
+            B.fsdp_flatten_shard(cu, [a], 0, b)
+            b.copy_(a)
+        torch.cuda.synchronize()
+        probe = {}
+        for name, fn in (("library_copy", lambda: B.fsdp_flatten_shard(cu, [a], 0, b)),
+                         ("hipMemcpyDtoD", lambda: b.copy_(a))):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            probe[name] = {"bytes": 8 * n, "ms": round(ms, 4),
+                           "GB/s": round(8 * n / (ms * 1e-3) / 1e9, 1)}
+        result["copy_ceiling"] = probe
+        del a, b
+
+    if not args.no_cpu_baseline:
+        host = {
+            "params": [p.cpu().numpy() for p in params],
+            "gathered": gathered.cpu().numpy(),
+            "contribs": contribs[:, : S // 8].contiguous().view(torch.int16).cpu().numpy()
+                        .view(np.uint16),
+            "adam_p": adam_p.cpu().numpy(),
+            "adam_g": grad.cpu().numpy(),
+        }
+        result["cpu_baseline"] = cpu_baseline(host, unit, N, k, S, valid, pre, post, hp,
+                                              rows=layout == B.FSDP_ROWS)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

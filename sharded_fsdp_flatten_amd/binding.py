@@ -21,7 +21,9 @@ STATUS_NAMES = {0: "FSDP_OK", 1: "FSDP_E_ARG", 2: "FSDP_E_RANGE", 3: "FSDP_E_ALI
                 4: "FSDP_E_OVERFLOW", 5: "FSDP_E_NOMEM", 6: "FSDP_E_HIP",
                 7: "FSDP_E_UNSUPPORTED"}
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfsdpflat.so")
+# The in-tree library; FSDP_FLATTEN_LIB may name another build of the same ABI.
+LIB_PATH = os.environ.get("FSDP_FLATTEN_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfsdpflat.so")
 
 
 class FsdpError(RuntimeError):
