@@ -69,6 +69,19 @@ def _load():
         lib.orc_adamw.argtypes = [_i64, _p, _p, _p, _p, ctypes.c_double, ctypes.c_double,
                                   ctypes.c_double, ctypes.c_double, ctypes.c_double, _i64, _p]
         lib.orc_adamw.restype = None
+        lib.orc_flat_shard_u16.argtypes = [_i32, _p, _p, _i64, _i64, _p]
+        lib.orc_flat_shard_u16.restype = ctypes.c_int
+        lib.orc_flat_copyout_u16.argtypes = [_i32, _p, _p, _p]
+        lib.orc_flat_copyout_u16.restype = None
+        lib.orc_rows_shard_u16.argtypes = [_i32, _p, _p, _p, _i64, _i64, _p]
+        lib.orc_rows_shard_u16.restype = ctypes.c_int
+        lib.orc_rows_copyout_u16.argtypes = [_i32, _p, _p, _i64, _p, _p]
+        lib.orc_rows_copyout_u16.restype = None
+        lib.orc_grad_reduce_ex.argtypes = [_i64, _i64, _p, ctypes.c_float, ctypes.c_float, _i64,
+                                           ctypes.c_int, _p]
+        lib.orc_grad_reduce_ex.restype = None
+        lib.orc_grad_accumulate.argtypes = [_i64, _p, _p, ctypes.c_int]
+        lib.orc_grad_accumulate.restype = None
         _lib = lib
     return _lib
 
@@ -226,3 +239,94 @@ def adamw(p: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, *, lr: flo
     _load().orc_adamw(n, _ptr(p), _ptr(g), _ptr(m), _ptr(v), lr, betas[0], betas[1], eps,
                       weight_decay, step, _ptr(pb) if pb is not None else None)
     return pb
+
+
+# --------------------------------------------------------------------------
+# 16-bit layouts, hybrid / accumulating reduction, local accumulation
+# --------------------------------------------------------------------------
+
+def _u16(a) -> np.ndarray:
+    return np.ascontiguousarray(a, dtype=np.uint16)
+
+
+def flat_shard_u16(params: Sequence[np.ndarray], N: int, k: int) -> np.ndarray:
+    """FlatParameter shard of 16-bit (bf16 bit pattern) parameters (k = -1: all ranks)."""
+    params = [_u16(p).reshape(-1) for p in params]
+    n = _i64_array(p.size for p in params)
+    T, S, L, pad = flat_sizes(n, N)
+    out = np.empty(L if k < 0 else S, dtype=np.uint16)
+    ptrs = _ptr_array(params)
+    if _load().orc_flat_shard_u16(len(params), _ptr(n), _ptr(ptrs), N, k, _ptr(out)) != 0:
+        raise MemoryError("oracle flat_shard_u16: allocation failed")
+    return out
+
+
+def flat_copyout_u16(shapes: Sequence[Sequence[int]], gathered: np.ndarray) -> list:
+    g = _u16(gathered).reshape(-1)
+    n = _i64_array(numel(s) for s in shapes)
+    if int(n.sum()) > g.size:
+        raise ValueError("gathered buffer shorter than the unit")
+    outs = [np.empty(tuple(s), dtype=np.uint16) for s in shapes]
+    ptrs = _ptr_array(outs)
+    _load().orc_flat_copyout_u16(len(outs), _ptr(n), _ptr(g), _ptr(ptrs))
+    return outs
+
+
+def rows_shard_u16(params: Sequence[np.ndarray], N: int, k: int) -> np.ndarray:
+    shapes = [p.shape for p in params]
+    flat = [_u16(p).reshape(-1) for p in params]
+    mr = [rows_of(s) for s in shapes]
+    m = _i64_array(a for a, _ in mr)
+    r = _i64_array(b for _, b in mr)
+    P_r = rows_sizes(shapes, N)
+    out = np.empty(N * P_r if k < 0 else P_r, dtype=np.uint16)
+    ptrs = _ptr_array(flat)
+    _load().orc_rows_shard_u16(len(flat), _ptr(m), _ptr(r), _ptr(ptrs), N, k, _ptr(out))
+    return out
+
+
+def rows_copyout_u16(shapes: Sequence[Sequence[int]], N: int, gathered: np.ndarray) -> list:
+    g = _u16(gathered).reshape(-1)
+    P_r = rows_sizes(shapes, N)
+    if g.size < N * P_r:
+        raise ValueError("gathered buffer shorter than N*P_r")
+    mr = [rows_of(s) for s in shapes]
+    m = _i64_array(a for a, _ in mr)
+    r = _i64_array(b for _, b in mr)
+    outs = [np.empty(tuple(s), dtype=np.uint16) for s in shapes]
+    ptrs = _ptr_array(outs)
+    _load().orc_rows_copyout_u16(len(outs), _ptr(m), _ptr(r), N, _ptr(g), _ptr(ptrs))
+    return outs
+
+
+def grad_reduce_ex(contribs: Sequence[np.ndarray], pre: float = 1.0, post: float = 1.0,
+                   group: int = 0, out: np.ndarray = None) -> np.ndarray:
+    """Reduction in groups of `group` consecutive ranks (0: one group of all N).  With `out`
+    given, the fresh result is added to it in place (accumulation) and `out` is returned."""
+    cs = [np.ascontiguousarray(c, dtype=np.uint16).reshape(-1) for c in contribs]
+    N = len(cs)
+    g = N if group == 0 else group
+    if N == 0 or N % g != 0:
+        raise ValueError("the group size must divide the number of contributions")
+    length = cs[0].size
+    if any(c.size != length for c in cs):
+        raise ValueError("contributions differ in length")
+    acc = out is not None
+    if acc:
+        if out.dtype != np.float32 or out.size != length or not out.flags["C_CONTIGUOUS"]:
+            raise ValueError("out must be a contiguous float32 array of the contribution length")
+        res = out
+    else:
+        res = np.empty(length, dtype=np.float32)
+    ptrs = _ptr_array(cs)
+    _load().orc_grad_reduce_ex(N, length, _ptr(ptrs), pre, post, g, 1 if acc else 0, _ptr(res))
+    return res
+
+
+def grad_accumulate(grad_bf16: np.ndarray, acc: np.ndarray, init: bool) -> np.ndarray:
+    """acc = (init ? 0 : acc) + fp32(grad), in place on the float32 accumulator."""
+    g = _u16(grad_bf16).reshape(-1)
+    if acc.dtype != np.float32 or acc.size != g.size or not acc.flags["C_CONTIGUOUS"]:
+        raise ValueError("acc must be a contiguous float32 array of the gradient's length")
+    _load().orc_grad_accumulate(g.size, _ptr(g), _ptr(acc), 1 if init else 0)
+    return acc

@@ -306,3 +306,131 @@ void orc_adamw(int64_t len, float* p, const float* g, float* m, float* v, double
         if (pb) pb[j] = orc_bf16(pj);
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* 16-bit layouts (bf16 parameters and gradients moved without arithmetic)  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The same FlatParameter and FSDP2 layouts as above, for 16-bit elements:
+ * casting before the AllGather moves bf16 parameters ([P1] section 3.4,
+ * "Native Mixed Precision": collectives in low precision; [P2] section 5:
+ * FSDP2 all-gathers bf16 parameters), and the ReduceScatter input is the
+ * unsharded bf16 gradient laid out like the FlatParameter ([P1] section 3.4,
+ * "Communication layout").  Padding is the bit pattern 0x0000 (+0.0).
+ */
+int orc_flat_shard_u16(int32_t p, const int64_t* numel, const uint16_t* const* params, int64_t N,
+                       int64_t k, uint16_t* out) {
+    int64_t sz[4];
+    orc_flat_sizes(p, numel, N, sz);
+    int64_t L = sz[2], S = sz[1];
+    uint16_t* F = (uint16_t*)malloc((size_t)(L > 0 ? L : 1) * sizeof(uint16_t));
+    if (!F) return -1;
+    int64_t w = 0;
+    for (int32_t i = 0; i < p; ++i)
+        for (int64_t j = 0; j < numel[i]; ++j) F[w++] = params[i][j];
+    while (w < L) F[w++] = 0;
+    if (k < 0) {
+        for (int64_t j = 0; j < L; ++j) out[j] = F[j];
+    } else {
+        for (int64_t j = 0; j < S; ++j) out[j] = F[k * S + j];
+    }
+    free(F);
+    return 0;
+}
+
+void orc_flat_copyout_u16(int32_t p, const int64_t* numel, const uint16_t* gathered,
+                          uint16_t* const* outs) {
+    int64_t off = 0;
+    for (int32_t i = 0; i < p; ++i) {
+        for (int64_t j = 0; j < numel[i]; ++j) outs[i][j] = gathered[off + j];
+        off += numel[i];
+    }
+}
+
+int orc_rows_shard_u16(int32_t p, const int64_t* m, const int64_t* r, const uint16_t* const* params,
+                       int64_t N, int64_t k, uint16_t* out) {
+    int64_t k_lo = k < 0 ? 0 : k, k_hi = k < 0 ? N : k + 1;
+    int64_t w = 0;
+    for (int64_t kk = k_lo; kk < k_hi; ++kk) {
+        for (int32_t i = 0; i < p; ++i) {
+            int64_t c = ceil_div(m[i], N);
+            int64_t row_lo = min64(m[i], kk * c);
+            int64_t row_hi = min64(m[i], (kk + 1) * c);
+            for (int64_t e = row_lo * r[i]; e < row_hi * r[i]; ++e) out[w++] = params[i][e];
+            for (int64_t e = (row_hi - row_lo) * r[i]; e < c * r[i]; ++e) out[w++] = 0;
+        }
+    }
+    return 0;
+}
+
+void orc_rows_copyout_u16(int32_t p, const int64_t* m, const int64_t* r, int64_t N,
+                          const uint16_t* gathered, uint16_t* const* outs) {
+    int64_t P_r;
+    orc_rows_sizes(p, m, r, N, &P_r);
+    for (int32_t i = 0; i < p; ++i) {
+        int64_t q = 0;
+        for (int32_t j = 0; j < i; ++j) q += ceil_div(m[j], N) * r[j];
+        int64_t c = ceil_div(m[i], N);
+        int64_t w = 0;
+        for (int64_t kk = 0; kk < N; ++kk) {
+            int64_t row_lo = min64(m[i], kk * c);
+            int64_t row_hi = min64(m[i], (kk + 1) * c);
+            const uint16_t* seg = gathered + kk * P_r + q;
+            for (int64_t e = 0; e < (row_hi - row_lo) * r[i]; ++e) outs[i][w++] = seg[e];
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Gradient reduction with hybrid groups and accumulation                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Hybrid sharding ([P1] section 3.4, "Sharding Strategies", the sum over all
+ * W ranks equals the sum over the W/F sharding groups of the in-group sums):
+ * the N ranks form N/F groups of F consecutive ranks; each group's terms are
+ * summed first (the ReduceScatter inside the sharding group), then the group
+ * sums (the AllReduce across replicas).  Reading taken for the order: both
+ * levels sequential, in rank and group order, each starting from its first
+ * term.  group == N is the flat reduction; so is group == 1.
+ *
+ * Gradient accumulation with communication ([P1] section 3.4 "Communication
+ * Optimizations: Overlapping, Prefetching, and Accumulation", "Gradient
+ * Accumulation Variants": every micro-batch is still reduced, and each rank
+ * accumulates its sharded gradient): when `accumulate` is non-zero the
+ * existing shard value is kept and the fresh reduction (already divided by
+ * post) is added to it, out = out + fresh.
+ */
+void orc_grad_reduce_ex(int64_t N, int64_t len, const uint16_t* const* contribs, float pre,
+                        float post, int64_t group, int accumulate, float* out) {
+    for (int64_t j = 0; j < len; ++j) {
+        float total = 0.0f;
+        for (int64_t g = 0; g < N / group; ++g) {
+            float s = orc_bf16_to_f32(contribs[g * group][j]) / pre;
+            for (int64_t r = g * group + 1; r < (g + 1) * group; ++r) {
+                float term = orc_bf16_to_f32(contribs[r][j]) / pre;
+                s = s + term;
+            }
+            total = (g == 0) ? s : total + s;
+        }
+        float fresh = total / post;
+        out[j] = accumulate ? out[j] + fresh : fresh;
+    }
+}
+
+/*
+ * Gradient accumulation without communication ([P1] section 3.4,
+ * "Gradient Accumulation Variants": each rank accumulates the unsharded
+ * gradients locally and the reduction runs only on the last micro-batch): the
+ * micro-batch's bf16 gradient is widened exactly and added to an fp32
+ * accumulator; init != 0 starts the accumulator from this gradient.  The pages
+ * do not give the accumulator's precision; fp32 (the reduction precision) is
+ * taken.
+ */
+void orc_grad_accumulate(int64_t n, const uint16_t* grad, float* acc, int init) {
+    for (int64_t j = 0; j < n; ++j) {
+        float g = orc_bf16_to_f32(grad[j]);
+        acc[j] = init ? g : acc[j] + g;
+    }
+}
