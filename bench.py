@@ -49,6 +49,9 @@ def parse_args():
     ap.add_argument("--contribs", default="stacked", choices=["stacked", "separate"],
                     help="gradient contributions as one [N, S] receive buffer (default) or as "
                          "N separate allocations")
+    ap.add_argument("--next", action="store_true",
+                    help="also time the next rows (hybrid + accumulating reduce, bf16 copy-in, "
+                         "cast, bf16 copy-out, local accumulation) in a second cold-cache loop")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 4 GiB fp32 copy through the library (N = 1 unit) "
                          "and hipMemcpy device-to-device, as copy ceilings")
@@ -143,6 +146,57 @@ def cpu_baseline(host, unit, N, k, S, valid, pre, post, hp, rows):
         "per_kernel_gbs": {name: round(b / dt / 1e9, 3) for name, (b, dt) in parts.items()},
         "seconds": round(t_tot, 2),
     }
+
+
+def time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows, grad, outs,
+                   gathered, adam_p, stream):
+    """The next rows, in an order where no kernel reads what the previous one just wrote:
+    hybrid reduction (groups of 8 ranks) accumulating into the grad shard; copy-in of
+    per-parameter bf16 gradients into the ReduceScatter input (all ranks); cast of rank k's
+    fp32 shard to bf16; bf16 copy-out of a gathered bf16 unit; local fp32 accumulation of an
+    unsharded bf16 gradient.  Reuses the step's buffers as inputs (values do not matter)."""
+    import torch
+    dev = grad.device
+    rs_input = torch.empty(L, dtype=torch.bfloat16, device=dev)
+    shard16 = torch.empty(S, dtype=torch.bfloat16, device=dev)
+    group = 8 if N % 8 == 0 and N > 8 else 0
+    rows = {
+        "grad_reduce_hybrid_accumulate": (lambda: B.fsdp_grad_reduce_shard_ex(
+            u, contrib_rows, pre, post, grad, group=group, accumulate=True), (2 * N + 8) * S, S),
+        "copyin_bf16_all_ranks": (lambda: B.fsdp_flatten_shard_bf16(
+            u, outs, B.FSDP_ALL_RANKS, rs_input), 2 * T + 2 * L, L),
+        "cast_to_bf16_rank": (lambda: B.fsdp_cast_to_bf16(u, k, adam_p, shard16), 6 * S, S),
+        "copyout_bf16": (lambda: B.fsdp_unflatten_copyout_bf16(u, rs_input, outs), 4 * T, T),
+        "grad_accumulate_all": (lambda: B.fsdp_grad_accumulate(
+            u, B.FSDP_ALL_RANKS, rs_input, gathered, False), 10 * L, L),
+    }
+    order = list(rows)
+    for _ in range(max(1, args.warmup)):
+        for n in order:
+            rows[n][0]()
+    torch.cuda.synchronize()
+    ev = {n: [] for n in order}
+    reps = max(5, args.steps // 5)
+    for _ in range(reps):
+        for n in order:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rows[n][0]()
+            e1.record(stream)
+            ev[n].append((e0, e1))
+    torch.cuda.synchronize()
+    out = {}
+    for n in order:
+        ms = sum(a.elapsed_time(b) for a, b in ev[n]) / reps
+        fn, nbytes, elems = rows[n]
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[n] = {"ms": round(ms, 4), "bytes": nbytes, "GB/s": round(gbs, 1),
+                  "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+                  "elements_per_s": float("%.4g" % (elems / (ms * 1e-3))), "reps": reps}
+    out["hybrid_group"] = group
+    del rs_input, shard16
+    return out
 
 
 def main():
@@ -276,6 +330,10 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
     }
+
+    if args.next:
+        result["next_rows"] = time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows,
+                                             grad, outs, gathered, adam_p, stream)
 
     if args.copy_probe:
         n = 1 << 30

@@ -117,6 +117,17 @@ typedef struct {
     int64_t step;          /* t >= 1: the step being taken (1 for the first)   */
 } fsdp_adamw_cfg;
 
+/* Options of fsdp_grad_reduce_shard_ex. */
+typedef struct {
+    float pre_divide;      /* finite, non-zero: divides every term before it is added     */
+    float post_divide;     /* finite, non-zero: divides the total                         */
+    int32_t group;         /* ranks per sharding group (hybrid sharding).  0, 1 or N: one
+                              flat sequential sum.  Otherwise it must divide N and be at
+                              most 128                                                    */
+    int32_t accumulate;    /* non-zero: add the result to what grad_shard already holds
+                              (N <= 128)                                                  */
+} fsdp_reduce_opts;
+
 /* Version of this header the library was built from (FSDP_ABI_VERSION). */
 FSDP_API int32_t fsdp_abi_version(void);
 
@@ -216,6 +227,77 @@ FSDP_API fsdp_status fsdp_grad_reduce_shard(const fsdp_unit* unit, const uint16_
 FSDP_API fsdp_status fsdp_adam_shard(const fsdp_unit* unit, float* param, const float* grad,
                             float* exp_avg, float* exp_avg_sq, const fsdp_adamw_cfg* cfg,
                             uint16_t* param_bf16, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Beyond the four calls: casting before the gather, the FSDP2 copy-in,
+ * gradient accumulation and hybrid sharding.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * Cast fp32 to bf16 (round to nearest even, NaN kept NaN) over rank k's shard
+ * (S elements) or, with k == FSDP_ALL_RANKS, over the whole gathered / unsharded
+ * layout (L elements).  The pages cast the full-precision shard to low
+ * precision once per FlatParameter and all-gather the low-precision copy
+ * ([P1] section 3.4, "Native Mixed Precision and the Sharded Gradient Scaler";
+ * [P2] section 5: FSDP2 all-gathers bf16 parameters); the same cast turns an
+ * fp32-accumulated gradient into the bf16 ReduceScatter input.
+ *   src : device pointer, fp32.   dst : device pointer, bf16 (same count).
+ */
+FSDP_API fsdp_status fsdp_cast_to_bf16(const fsdp_unit* unit, int32_t k, const float* src,
+                                       uint16_t* dst, void* stream);
+
+/*
+ * Copy a gathered bf16 unit (the AllGather of bf16 shards: L elements, FLAT
+ * padding never read, or N*P_r for ROWS) out into per-parameter bf16 tensors --
+ * the copy-out of fsdp_unflatten_copyout when the cast happened before the
+ * gather.  Bit-identical to casting after the gather.
+ *   gathered : device pointer, bf16.   outs : host array of n_params device
+ *   pointers, bf16, numel_i each (NULL allowed for zero-size parameters).
+ */
+FSDP_API fsdp_status fsdp_unflatten_copyout_bf16(const fsdp_unit* unit, const uint16_t* gathered,
+                                                 uint16_t* const* outs, void* stream);
+
+/*
+ * fsdp_flatten_shard for bf16 tensors.  With k == FSDP_ALL_RANKS on the
+ * per-parameter bf16 gradients this is the FSDP2 copy-in: it writes the
+ * ReduceScatter input, every rank's segment in rank order with each
+ * parameter's rows padded to c_i rows by zeros ([P2] section 3: gradients
+ * reduce-scatter per parameter; [P1] section 3.4, "Communication layout":
+ * the unsharded gradient in the FlatParameter layout for FSDP1).
+ *   params : host array of n_params device pointers, bf16.
+ *   shard  : device pointer, bf16, S elements (L for FSDP_ALL_RANKS).
+ */
+FSDP_API fsdp_status fsdp_flatten_shard_bf16(const fsdp_unit* unit, const uint16_t* const* params,
+                                             int32_t k, uint16_t* shard, void* stream);
+
+/*
+ * fsdp_grad_reduce_shard with hybrid sharding and accumulation.
+ * Hybrid sharding ([P1] section 3.4, "Sharding Strategies": a ReduceScatter
+ * inside each sharding group, then an AllReduce across the replication
+ * groups; the sum over all ranks equals the sum of the group sums): the N
+ * contributions form N/group groups of consecutive ranks; each group is summed
+ * in rank order, then the group sums in group order; then / post_divide.
+ * Accumulation with communication ([P1] section 3.4, "Communication
+ * Optimizations: Overlapping, Prefetching, and Accumulation", "Gradient
+ * Accumulation Variants"): out = out + result.
+ * Errors as fsdp_grad_reduce_shard, plus FSDP_E_ARG (opts NULL), FSDP_E_RANGE
+ * (group does not divide N) and FSDP_E_UNSUPPORTED (group > 128 with
+ * group < N, or accumulate with N > 128).
+ */
+FSDP_API fsdp_status fsdp_grad_reduce_shard_ex(const fsdp_unit* unit, const uint16_t* const* contribs,
+                                               const fsdp_reduce_opts* opts, float* grad_shard,
+                                               void* stream);
+
+/*
+ * Gradient accumulation without communication ([P1] section 3.4, "Gradient
+ * Accumulation Variants": each rank accumulates the unsharded gradient
+ * locally and reduces once, on the last micro-batch):
+ * acc[j] = (init ? 0 : acc[j]) + fp32(grad[j]) over rank k's shard (S elements)
+ * or, with k == FSDP_ALL_RANKS, the whole unsharded layout (L elements).
+ *   grad : device pointer, bf16.   acc : device pointer, fp32, updated in place.
+ */
+FSDP_API fsdp_status fsdp_grad_accumulate(const fsdp_unit* unit, int32_t k, const uint16_t* grad,
+                                          float* acc, int32_t init, void* stream);
 
 #ifdef __cplusplus
 }

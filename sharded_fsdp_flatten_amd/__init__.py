@@ -12,11 +12,16 @@ from .binding import (  # noqa: F401
     Unit,
     fsdp_abi_version,
     fsdp_adam_shard,
+    fsdp_cast_to_bf16,
     fsdp_flatten_shard,
+    fsdp_flatten_shard_bf16,
+    fsdp_grad_accumulate,
     fsdp_grad_reduce_shard,
+    fsdp_grad_reduce_shard_ex,
     fsdp_last_error,
     fsdp_status_string,
     fsdp_unflatten_copyout,
+    fsdp_unflatten_copyout_bf16,
     fsdp_unit_create,
     fsdp_unit_destroy,
     fsdp_unit_info,

@@ -49,6 +49,11 @@ class fsdp_adamw_cfg(ctypes.Structure):
                 ("step", ctypes.c_int64)]
 
 
+class fsdp_reduce_opts(ctypes.Structure):
+    _fields_ = [("pre_divide", ctypes.c_float), ("post_divide", ctypes.c_float),
+                ("group", ctypes.c_int32), ("accumulate", ctypes.c_int32)]
+
+
 _lib = None
 _vp = ctypes.c_void_p
 
@@ -87,6 +92,16 @@ def load() -> ctypes.CDLL:
     lib.fsdp_adam_shard.argtypes = [_vp, _vp, _vp, _vp, _vp, ctypes.POINTER(fsdp_adamw_cfg), _vp,
                                     _vp]
     lib.fsdp_adam_shard.restype = st
+    lib.fsdp_cast_to_bf16.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp]
+    lib.fsdp_cast_to_bf16.restype = st
+    lib.fsdp_unflatten_copyout_bf16.argtypes = [_vp, _vp, _vp, _vp]
+    lib.fsdp_unflatten_copyout_bf16.restype = st
+    lib.fsdp_flatten_shard_bf16.argtypes = [_vp, _vp, ctypes.c_int32, _vp, _vp]
+    lib.fsdp_flatten_shard_bf16.restype = st
+    lib.fsdp_grad_reduce_shard_ex.argtypes = [_vp, _vp, ctypes.POINTER(fsdp_reduce_opts), _vp, _vp]
+    lib.fsdp_grad_reduce_shard_ex.restype = st
+    lib.fsdp_grad_accumulate.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp]
+    lib.fsdp_grad_accumulate.restype = st
     _lib = lib
     return lib
 
@@ -281,7 +296,70 @@ def fsdp_adam_shard(unit: Unit, param, grad, exp_avg, exp_avg_sq, *, lr: float,
                                   _stream(stream, param, grad, exp_avg, exp_avg_sq)))
 
 
+def fsdp_cast_to_bf16(unit: Unit, k: int, src, dst, stream=None) -> None:
+    """bf16(src) over rank k's shard (S elements) or, k = FSDP_ALL_RANKS, the L-element layout."""
+    n = unit.L if k == FSDP_ALL_RANKS else unit.S
+    _need(src, n, "src")
+    _need(dst, n, "dst")
+    _check(load().fsdp_cast_to_bf16(unit.handle, k, _addr(src, _F32) or None,
+                                    _addr(dst, _BF16) or None, _stream(stream, src, dst)))
+
+
+def fsdp_unflatten_copyout_bf16(unit: Unit, gathered, outs: Sequence, stream=None) -> None:
+    """Copy a gathered bf16 unit out into per-parameter bf16 tensors (cast before gather)."""
+    if len(outs) != len(unit.shapes):
+        raise ValueError("need %d outputs, got %d" % (len(unit.shapes), len(outs)))
+    for i, o in enumerate(outs):
+        _need(o, unit.numels[i], "outs[%d]" % i, exact=True)
+    _need(gathered, unit.L, "gathered")
+    table = _ptr_table(outs, _BF16)
+    _check(load().fsdp_unflatten_copyout_bf16(unit.handle, _addr(gathered, _BF16) or None,
+                                              ctypes.cast(table, _vp),
+                                              _stream(stream, gathered, *outs)))
+
+
+def fsdp_flatten_shard_bf16(unit: Unit, params: Sequence, k: int, shard, stream=None) -> None:
+    """fsdp_flatten_shard for bf16 tensors (k = FSDP_ALL_RANKS on gradients: the copy-in)."""
+    if len(params) != len(unit.shapes):
+        raise ValueError("need %d tensors, got %d" % (len(unit.shapes), len(params)))
+    for i, p in enumerate(params):
+        _need(p, unit.numels[i], "params[%d]" % i, exact=True)
+    _need(shard, unit.L if k == FSDP_ALL_RANKS else unit.S, "shard")
+    table = _ptr_table(params, _BF16)
+    _check(load().fsdp_flatten_shard_bf16(unit.handle, ctypes.cast(table, _vp), k,
+                                          _addr(shard, _BF16) or None,
+                                          _stream(stream, shard, *params)))
+
+
+def fsdp_grad_reduce_shard_ex(unit: Unit, contribs: Sequence, pre_divide: float,
+                              post_divide: float, grad_shard, *, group: int = 0,
+                              accumulate: bool = False, stream=None) -> None:
+    """Reduction in hybrid groups of `group` ranks, optionally accumulating into grad_shard."""
+    if len(contribs) != unit.N:
+        raise ValueError("need exactly N = %d contributions, got %d" % (unit.N, len(contribs)))
+    for r, c in enumerate(contribs):
+        _need(c, unit.S, "contribs[%d]" % r)
+    _need(grad_shard, unit.S, "grad_shard")
+    table = _ptr_table(contribs, _BF16)
+    opts = fsdp_reduce_opts(float(pre_divide), float(post_divide), int(group),
+                            1 if accumulate else 0)
+    _check(load().fsdp_grad_reduce_shard_ex(unit.handle, ctypes.cast(table, _vp),
+                                            ctypes.byref(opts), _addr(grad_shard, _F32) or None,
+                                            _stream(stream, grad_shard, *contribs)))
+
+
+def fsdp_grad_accumulate(unit: Unit, k: int, grad, acc, init: bool, stream=None) -> None:
+    """acc = (init ? 0 : acc) + fp32(grad) over rank k's shard or (FSDP_ALL_RANKS) all L."""
+    n = unit.L if k == FSDP_ALL_RANKS else unit.S
+    _need(grad, n, "grad")
+    _need(acc, n, "acc")
+    _check(load().fsdp_grad_accumulate(unit.handle, k, _addr(grad, _BF16) or None,
+                                       _addr(acc, _F32) or None, 1 if init else 0,
+                                       _stream(stream, grad, acc)))
+
+
 ABI_FUNCTIONS = ["fsdp_abi_version", "fsdp_last_error", "fsdp_status_string", "fsdp_unit_create",
                  "fsdp_unit_destroy", "fsdp_unit_info", "fsdp_unit_param_offset",
                  "fsdp_flatten_shard", "fsdp_unflatten_copyout", "fsdp_grad_reduce_shard",
-                 "fsdp_adam_shard"]
+                 "fsdp_adam_shard", "fsdp_cast_to_bf16", "fsdp_unflatten_copyout_bf16",
+                 "fsdp_flatten_shard_bf16", "fsdp_grad_reduce_shard_ex", "fsdp_grad_accumulate"]

@@ -69,6 +69,47 @@ fsdp_status check_buf(const void* p, int64_t count, size_t elem, const char* nam
     return FSDP_OK;
 }
 
+constexpr int64_t kMaxRanksPerLaunch = 128;  // contribution pointers one kernel launch holds
+
+fsdp_status reduce_impl(const fsdp_unit* unit, const uint16_t* const* contribs,
+                        const fsdp_reduce_opts* opts, float* grad_shard, void* stream,
+                        const char* who) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    if (!opts) return fail(FSDP_E_ARG, "opts is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    const float pre = opts->pre_divide, post = opts->post_divide;
+    if (!std::isfinite(pre) || pre == 0.0f)
+        return fail(FSDP_E_RANGE, "pre_divide must be finite and non-zero");
+    if (!std::isfinite(post) || post == 0.0f)
+        return fail(FSDP_E_RANGE, "post_divide must be finite and non-zero");
+    int64_t group = opts->group;
+    if (group < 0 || group > u.N) return fail(FSDP_E_RANGE, "group must be in [0, N]");
+    if (group == 0) group = u.N;
+    if (u.N % group != 0) return fail(FSDP_E_RANGE, "group must divide N");
+    if (group > 1 && group < u.N && group > kMaxRanksPerLaunch)
+        return fail(FSDP_E_UNSUPPORTED, "hybrid groups of more than 128 ranks");
+    if (opts->accumulate && u.N > kMaxRanksPerLaunch)
+        return fail(FSDP_E_UNSUPPORTED, "accumulation over more than 128 ranks");
+    fsdp_status s;
+    if ((s = check_ptr_table(reinterpret_cast<const void* const*>(contribs),
+                             static_cast<size_t>(u.N), nullptr, u.S, sizeof(uint16_t),
+                             "contribs")) != FSDP_OK)
+        return s;
+    if ((s = check_buf(grad_shard, u.S, sizeof(float), "grad_shard")) != FSDP_OK) return s;
+    if (u.S == 0) return ok();
+    const hipError_t e =
+        fsdp::launch_grad_reduce(contribs, u.N, u.S, pre, post, group, opts->accumulate != 0,
+                                 grad_shard, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, (std::string(who) + " launch").c_str());
+    return ok();
+}
+
+fsdp_status check_rank(const fsdp::UnitPlan& u, int32_t k) {
+    if (k != FSDP_ALL_RANKS && (k < 0 || k >= u.N))
+        return fail(FSDP_E_RANGE, "k must be in [0, N) or FSDP_ALL_RANKS");
+    return FSDP_OK;
+}
+
 std::vector<int64_t> param_numels(const fsdp::UnitPlan& u) {
     std::vector<int64_t> n;
     n.reserve(u.params.size());
@@ -164,9 +205,10 @@ fsdp_status fsdp_flatten_shard(const fsdp_unit* unit, const float* const* params
     if ((s = check_buf(shard, out_len, sizeof(float), "shard")) != FSDP_OK) return s;
     if (out_len == 0) return ok();
     std::vector<fsdp::CopySeg> segs;
-    fsdp::plan_flatten(u, params, k, shard, &segs);
+    fsdp::plan_flatten(u, reinterpret_cast<const void* const*>(params), k, shard, sizeof(float),
+                       &segs);
     const hipError_t e =
-        fsdp::launch_segcopy(segs, fsdp::OutType::kF32, static_cast<hipStream_t>(stream));
+        fsdp::launch_segcopy(segs, fsdp::Pipe::kF32toF32, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fsdp_flatten_shard launch");
     return ok();
 }
@@ -184,9 +226,10 @@ fsdp_status fsdp_unflatten_copyout(const fsdp_unit* unit, const float* gathered,
         return s;
     if (u.T == 0) return ok();
     std::vector<fsdp::CopySeg> segs;
-    fsdp::plan_copyout(u, gathered, outs, &segs);
+    fsdp::plan_copyout(u, gathered, sizeof(float), reinterpret_cast<void* const*>(outs),
+                       sizeof(uint16_t), &segs);
     const hipError_t e =
-        fsdp::launch_segcopy(segs, fsdp::OutType::kBF16, static_cast<hipStream_t>(stream));
+        fsdp::launch_segcopy(segs, fsdp::Pipe::kF32toBF16, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fsdp_unflatten_copyout launch");
     return ok();
 }
@@ -194,23 +237,14 @@ fsdp_status fsdp_unflatten_copyout(const fsdp_unit* unit, const float* gathered,
 fsdp_status fsdp_grad_reduce_shard(const fsdp_unit* unit, const uint16_t* const* contribs,
                                    float pre_divide, float post_divide, float* grad_shard,
                                    void* stream) {
-    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
-    const fsdp::UnitPlan& u = unit->plan;
-    if (!std::isfinite(pre_divide) || pre_divide == 0.0f)
-        return fail(FSDP_E_RANGE, "pre_divide must be finite and non-zero");
-    if (!std::isfinite(post_divide) || post_divide == 0.0f)
-        return fail(FSDP_E_RANGE, "post_divide must be finite and non-zero");
-    fsdp_status s;
-    if ((s = check_ptr_table(reinterpret_cast<const void* const*>(contribs),
-                             static_cast<size_t>(u.N), nullptr, u.S, sizeof(uint16_t),
-                             "contribs")) != FSDP_OK)
-        return s;
-    if ((s = check_buf(grad_shard, u.S, sizeof(float), "grad_shard")) != FSDP_OK) return s;
-    if (u.S == 0) return ok();
-    const hipError_t e = fsdp::launch_grad_reduce(contribs, u.N, u.S, pre_divide, post_divide,
-                                                  grad_shard, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) return hip_fail(e, "fsdp_grad_reduce_shard launch");
-    return ok();
+    const fsdp_reduce_opts opts{pre_divide, post_divide, 0, 0};
+    return reduce_impl(unit, contribs, &opts, grad_shard, stream, "fsdp_grad_reduce_shard");
+}
+
+fsdp_status fsdp_grad_reduce_shard_ex(const fsdp_unit* unit, const uint16_t* const* contribs,
+                                      const fsdp_reduce_opts* opts, float* grad_shard,
+                                      void* stream) {
+    return reduce_impl(unit, contribs, opts, grad_shard, stream, "fsdp_grad_reduce_shard_ex");
 }
 
 fsdp_status fsdp_adam_shard(const fsdp_unit* unit, float* param, const float* grad,
@@ -249,6 +283,83 @@ fsdp_status fsdp_adam_shard(const fsdp_unit* unit, float* param, const float* gr
     const hipError_t e = fsdp::launch_adamw(param, grad, exp_avg, exp_avg_sq, param_bf16, u.S, sc,
                                             static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fsdp_adam_shard launch");
+    return ok();
+}
+
+fsdp_status fsdp_cast_to_bf16(const fsdp_unit* unit, int32_t k, const float* src, uint16_t* dst,
+                              void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    fsdp_status s;
+    if ((s = check_rank(u, k)) != FSDP_OK) return s;
+    const int64_t n = k == FSDP_ALL_RANKS ? u.L : u.S;
+    if ((s = check_buf(src, n, sizeof(float), "src")) != FSDP_OK) return s;
+    if ((s = check_buf(dst, n, sizeof(uint16_t), "dst")) != FSDP_OK) return s;
+    if (n == 0) return ok();
+    std::vector<fsdp::CopySeg> segs;
+    fsdp::plan_whole(u, k, src, dst, &segs);
+    const hipError_t e =
+        fsdp::launch_segcopy(segs, fsdp::Pipe::kF32toBF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_cast_to_bf16 launch");
+    return ok();
+}
+
+fsdp_status fsdp_unflatten_copyout_bf16(const fsdp_unit* unit, const uint16_t* gathered,
+                                        uint16_t* const* outs, void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    const std::vector<int64_t> numels = param_numels(u);
+    fsdp_status s;
+    if ((s = check_buf(gathered, u.T > 0 ? u.L : 0, sizeof(uint16_t), "gathered")) != FSDP_OK)
+        return s;
+    if ((s = check_ptr_table(reinterpret_cast<const void* const*>(outs), numels.size(),
+                             numels.data(), 0, sizeof(uint16_t), "outs")) != FSDP_OK)
+        return s;
+    if (u.T == 0) return ok();
+    std::vector<fsdp::CopySeg> segs;
+    fsdp::plan_copyout(u, gathered, sizeof(uint16_t), reinterpret_cast<void* const*>(outs),
+                       sizeof(uint16_t), &segs);
+    const hipError_t e =
+        fsdp::launch_segcopy(segs, fsdp::Pipe::kBF16toBF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_unflatten_copyout_bf16 launch");
+    return ok();
+}
+
+fsdp_status fsdp_flatten_shard_bf16(const fsdp_unit* unit, const uint16_t* const* params,
+                                    int32_t k, uint16_t* shard, void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    fsdp_status s;
+    if ((s = check_rank(u, k)) != FSDP_OK) return s;
+    const int64_t out_len = k == FSDP_ALL_RANKS ? u.L : u.S;
+    const std::vector<int64_t> numels = param_numels(u);
+    if ((s = check_ptr_table(reinterpret_cast<const void* const*>(params), numels.size(),
+                             numels.data(), 0, sizeof(uint16_t), "params")) != FSDP_OK)
+        return s;
+    if ((s = check_buf(shard, out_len, sizeof(uint16_t), "shard")) != FSDP_OK) return s;
+    if (out_len == 0) return ok();
+    std::vector<fsdp::CopySeg> segs;
+    fsdp::plan_flatten(u, reinterpret_cast<const void* const*>(params), k, shard,
+                       sizeof(uint16_t), &segs);
+    const hipError_t e =
+        fsdp::launch_segcopy(segs, fsdp::Pipe::kBF16toBF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_flatten_shard_bf16 launch");
+    return ok();
+}
+
+fsdp_status fsdp_grad_accumulate(const fsdp_unit* unit, int32_t k, const uint16_t* grad,
+                                 float* acc, int32_t init, void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    fsdp_status s;
+    if ((s = check_rank(u, k)) != FSDP_OK) return s;
+    const int64_t n = k == FSDP_ALL_RANKS ? u.L : u.S;
+    if ((s = check_buf(grad, n, sizeof(uint16_t), "grad")) != FSDP_OK) return s;
+    if ((s = check_buf(acc, n, sizeof(float), "acc")) != FSDP_OK) return s;
+    if (n == 0) return ok();
+    const hipError_t e =
+        fsdp::launch_grad_accumulate(grad, acc, n, init != 0, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_grad_accumulate launch");
     return ok();
 }
 

@@ -10,17 +10,24 @@
 
 namespace fsdp {
 
-// Element type written by the segment-copy engine.
-enum class OutType { kF32, kBF16 };
+// Element types moved by the segment-copy engine: source -> destination.
+enum class Pipe { kF32toF32, kF32toBF16, kBF16toBF16 };
 
-// Execute planned segments (fp32 sources; fp32 or bf16 destinations; null
-// source = zero fill).  Splits into several launches if the table is larger
-// than one kernel argument block holds.
-hipError_t launch_segcopy(const std::vector<CopySeg>& segs, OutType out, hipStream_t stream);
+// Execute planned segments (null source = zero fill).  Splits into several
+// launches if the table is larger than one kernel argument block holds.
+hipError_t launch_segcopy(const std::vector<CopySeg>& segs, Pipe pipe, hipStream_t stream);
 
-// fp32 reduction of `n_contrib` bf16 contributions of `len` elements each.
+// fp32 reduction of `n_contrib` bf16 contributions of `len` elements each:
+// in groups of `group` consecutive ranks (group == n_contrib: one flat sum),
+// divided by pre (each term) and post (the total); with `accumulate` the
+// result is added to what `out` holds.
 hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib, int64_t len,
-                              float pre, float post, float* out, hipStream_t stream);
+                              float pre, float post, int64_t group, bool accumulate, float* out,
+                              hipStream_t stream);
+
+// acc = (init ? 0 : acc) + fp32(grad), elementwise over len.
+hipError_t launch_grad_accumulate(const uint16_t* grad, float* acc, int64_t len, bool init,
+                                  hipStream_t stream);
 
 // Derived AdamW scalars, each already rounded once to float on the host.
 struct AdamScalars {

@@ -56,11 +56,17 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #ifndef FSDP_BF16_VPL
 #define FSDP_BF16_VPL 2     // 4-element vectors per lane per tile, bf16 output
 #endif
+#ifndef FSDP_B16_VPL
+#define FSDP_B16_VPL 1      // 8-element vectors per lane per tile, bf16 -> bf16
+#endif
 #ifndef FSDP_REDUCE_THREADS
 #define FSDP_REDUCE_THREADS 64
 #endif
 #ifndef FSDP_REDUCE_AHEAD
 #define FSDP_REDUCE_AHEAD 8
+#endif
+#ifndef FSDP_ACC_NT
+#define FSDP_ACC_NT 1       // local accumulation: nt measured faster (5.9 vs 5.6 TB/s)
 #endif
 #ifndef FSDP_ADAM_THREADS
 #define FSDP_ADAM_THREADS 256
@@ -117,37 +123,58 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
     return static_cast<uint16_t>(pack_bf16x2(a, 0.0f) & 0xFFFFu);
 }
 
-// Output element traits.  A vector is 4 elements: one 16-byte fp32 load feeds
-// one 16-byte fp32 store or one 8-byte bf16 store.  kVpl vectors per lane make a
-// tile of kThreads * 4 * kVpl elements, lane l owning vectors l, l + kThreads, ...
-// so every load and store instruction is contiguous across the wave.
-template <typename OutT> struct Out;
-template <> struct Out<float> {
-    static constexpr int kVpl = FSDP_F32_VPL;
-    static constexpr int kAlign = 16;  // bytes a vector store needs
-    __device__ static void put(float* d, f4 x) { st4(d, x); }
+// Element pipes of the copy engine.  A vector is one 16-byte source load (4 fp32
+// or 8 bf16) and one store of the same element count (16 bytes, or 8 bytes for
+// fp32 -> bf16).  kVpl vectors per lane make a tile of kThreads * E * kVpl
+// elements, lane l owning vectors l, l + kThreads, ... so every load and store
+// instruction is contiguous across the wave.
+template <typename SrcT, typename DstT> struct Cp;
+template <> struct Cp<float, float> {
+    static constexpr int E = 4, kVpl = FSDP_F32_VPL;
+    static constexpr unsigned kDstAlign = 16;  // bytes a vector store needs
+    using V = f4;
+    __device__ static V load(const float* p) { return ld4(p); }
+    __device__ static V gather(const float* p) { return f4{p[0], p[1], p[2], p[3]}; }
+    __device__ static void put(float* d, V x) { st4(d, x); }
     __device__ static void put1(float* d, float x) { *d = x; }
     __device__ static void zero(float* d) { st4(d, f4{0.0f, 0.0f, 0.0f, 0.0f}); }
     __device__ static void zero1(float* d) { *d = 0.0f; }
 };
-template <> struct Out<uint16_t> {
-    static constexpr int kVpl = FSDP_BF16_VPL;
-    static constexpr int kAlign = 8;
-    __device__ static void put(uint16_t* d, f4 x) {
+template <> struct Cp<float, uint16_t> {
+    static constexpr int E = 4, kVpl = FSDP_BF16_VPL;
+    static constexpr unsigned kDstAlign = 8;
+    using V = f4;
+    __device__ static V load(const float* p) { return ld4(p); }
+    __device__ static V gather(const float* p) { return f4{p[0], p[1], p[2], p[3]}; }
+    __device__ static void put(uint16_t* d, V x) {
         stu2(d, u2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
     }
     __device__ static void put1(uint16_t* d, float x) { *d = to_bf16(x); }
     __device__ static void zero(uint16_t* d) { stu2(d, u2{0u, 0u}); }
     __device__ static void zero1(uint16_t* d) { *d = 0; }
 };
-template <typename OutT>
-constexpr int tile_elems() { return kThreads * 4 * Out<OutT>::kVpl; }
+template <> struct Cp<uint16_t, uint16_t> {
+    static constexpr int E = 8, kVpl = FSDP_B16_VPL;
+    static constexpr unsigned kDstAlign = 16;
+    using V = u4;
+    __device__ static V load(const uint16_t* p) { return ldu4(p); }
+    __device__ static V gather(const uint16_t* p) {
+        return u4{p[0] | (uint32_t{p[1]} << 16), p[2] | (uint32_t{p[3]} << 16),
+                  p[4] | (uint32_t{p[5]} << 16), p[6] | (uint32_t{p[7]} << 16)};
+    }
+    __device__ static void put(uint16_t* d, V x) { stu4(d, x); }
+    __device__ static void put1(uint16_t* d, uint16_t x) { *d = x; }
+    __device__ static void zero(uint16_t* d) { stu4(d, u4{0u, 0u, 0u, 0u}); }
+    __device__ static void zero1(uint16_t* d) { *d = 0; }
+};
+template <typename SrcT, typename DstT>
+constexpr int tile_elems() { return kThreads * Cp<SrcT, DstT>::E * Cp<SrcT, DstT>::kVpl; }
 
 // ---------------------------------------------------------------------------
 // segcopy
 // ---------------------------------------------------------------------------
 struct DevSeg {
-    const float* src;  // nullptr: zero fill
+    const void* src;  // nullptr: zero fill
     void* dst;
     int64_t blk_n, last_n, src_stride, dst_stride;
     uint32_t nblk, tiles_per_blk, tile0, unused;
@@ -160,79 +187,80 @@ struct SegTable {
 static_assert(sizeof(SegTable) <= 4096, "segment table must fit one kernel argument block");
 
 // n <= tile elements; s 16-byte aligned, d aligned for its vector store.
-template <typename OutT>
-__device__ __forceinline__ void tile_aligned(const float* __restrict__ s, OutT* __restrict__ d,
+template <typename SrcT, typename DstT>
+__device__ __forceinline__ void tile_aligned(const SrcT* __restrict__ s, DstT* __restrict__ d,
                                              int n) {
-    constexpr int kVpl = Out<OutT>::kVpl;
-    const int nv = n >> 2;
+    using P = Cp<SrcT, DstT>;
+    constexpr int E = P::E, kVpl = P::kVpl;
+    const int nv = n / E;
     if (nv == kThreads * kVpl) {  // full tile: all loads issued before any store
-        f4 x[kVpl];
+        typename P::V x[kVpl];
 #pragma unroll
-        for (int u = 0; u < kVpl; ++u) x[u] = ld4(s + 4 * (threadIdx.x + u * kThreads));
+        for (int u = 0; u < kVpl; ++u) x[u] = P::load(s + E * (threadIdx.x + u * kThreads));
 #pragma unroll
-        for (int u = 0; u < kVpl; ++u) Out<OutT>::put(d + 4 * (threadIdx.x + u * kThreads), x[u]);
+        for (int u = 0; u < kVpl; ++u) P::put(d + E * (threadIdx.x + u * kThreads), x[u]);
         return;
     }
-    for (int v = threadIdx.x; v < nv; v += kThreads) Out<OutT>::put(d + 4 * v, ld4(s + 4 * v));
-    for (int e = 4 * nv + threadIdx.x; e < n; e += kThreads) Out<OutT>::put1(d + e, s[e]);
+    for (int v = threadIdx.x; v < nv; v += kThreads) P::put(d + E * v, P::load(s + E * v));
+    for (int e = E * nv + threadIdx.x; e < n; e += kThreads) P::put1(d + e, s[e]);
 }
 
-// Elements of OutT from d up to the next boundary its vector store needs.
-template <typename OutT>
-__device__ __forceinline__ int head_to_align(const OutT* d) {
-    constexpr unsigned a = Out<OutT>::kAlign;
+// Elements of DstT from d up to the next boundary its vector store needs.
+template <typename SrcT, typename DstT>
+__device__ __forceinline__ int head_to_align(const DstT* d) {
+    constexpr unsigned a = Cp<SrcT, DstT>::kDstAlign;
     return static_cast<int>(((a - (reinterpret_cast<uintptr_t>(d) & (a - 1))) & (a - 1)) /
-                            sizeof(OutT));
+                            sizeof(DstT));
 }
 
-template <typename OutT>
-__device__ __forceinline__ void tile_zero(OutT* d, int n) {
-    const int h = min(head_to_align(d), n);
-    if (static_cast<int>(threadIdx.x) < h) Out<OutT>::zero1(d + threadIdx.x);
+template <typename SrcT, typename DstT>
+__device__ __forceinline__ void tile_zero(DstT* d, int n) {
+    using P = Cp<SrcT, DstT>;
+    constexpr int E = P::E;
+    const int h = min(head_to_align<SrcT, DstT>(d), n);
+    if (static_cast<int>(threadIdx.x) < h) P::zero1(d + threadIdx.x);
     d += h;
     n -= h;
-    const int nv = n >> 2;
-    for (int v = threadIdx.x; v < nv; v += kThreads) Out<OutT>::zero(d + 4 * v);
-    for (int e = 4 * nv + threadIdx.x; e < n; e += kThreads) Out<OutT>::zero1(d + e);
+    const int nv = n / E;
+    for (int v = threadIdx.x; v < nv; v += kThreads) P::zero(d + E * v);
+    for (int e = E * nv + threadIdx.x; e < n; e += kThreads) P::zero1(d + e);
 }
 
-// Any 4-byte-aligned source and element-aligned destination.  A short head of
-// scalar stores aligns the destination; if the source is then off a 16-byte
-// boundary by `shift` floats, the tile is loaded as aligned 128-bit vectors
-// (covering exactly the 16-byte blocks that hold the tile, so no access leaves
-// them) into LDS and re-read at the shift.  Tile-uniform control flow (barriers).
-template <typename OutT>
-__device__ __forceinline__ void tile_general(const float* s, OutT* d, int n, float* lds) {
-    const int h = min(head_to_align(d), n);
-    if (static_cast<int>(threadIdx.x) < h) Out<OutT>::put1(d + threadIdx.x, s[threadIdx.x]);
+// Any element-aligned source and destination.  A short head of scalar stores
+// aligns the destination; if the source is then off a 16-byte boundary by
+// `shift` elements, the tile is loaded as aligned 16-byte vectors (covering
+// exactly the 16-byte blocks that hold the tile, so no access leaves them) into
+// LDS and re-read at the shift.  Tile-uniform control flow (barriers).
+template <typename SrcT, typename DstT>
+__device__ __forceinline__ void tile_general(const SrcT* s, DstT* d, int n, SrcT* lds) {
+    using P = Cp<SrcT, DstT>;
+    constexpr int E = P::E;
+    const int h = min(head_to_align<SrcT, DstT>(d), n);
+    if (static_cast<int>(threadIdx.x) < h) P::put1(d + threadIdx.x, s[threadIdx.x]);
     s += h;
     d += h;
     n -= h;
-    const int shift = static_cast<int>((reinterpret_cast<uintptr_t>(s) & 15u) >> 2);
+    const int shift = static_cast<int>((reinterpret_cast<uintptr_t>(s) & 15u) / sizeof(SrcT));
     if (shift == 0) {
-        tile_aligned<OutT>(s, d, n);
+        tile_aligned<SrcT, DstT>(s, d, n);
         return;
     }
-    const float* base = s - shift;
-    const int nload = (shift + n + 3) >> 2;  // <= tile/4 + 2 vectors
+    const SrcT* base = s - shift;
+    const int nload = (shift + n + E - 1) / E;  // <= tile/E + 1 vectors
     for (int v = threadIdx.x; v < nload; v += kThreads)
-        *reinterpret_cast<f4*>(lds + 4 * v) = ld4(base + 4 * v);
+        *reinterpret_cast<typename P::V*>(lds + E * v) = P::load(base + E * v);
     __syncthreads();
-    const int nv = n >> 2;
-    for (int v = threadIdx.x; v < nv; v += kThreads) {
-        const float* x = lds + shift + 4 * v;
-        Out<OutT>::put(d + 4 * v, f4{x[0], x[1], x[2], x[3]});
-    }
-    for (int e = 4 * nv + threadIdx.x; e < n; e += kThreads)
-        Out<OutT>::put1(d + e, lds[shift + e]);
+    const int nv = n / E;
+    for (int v = threadIdx.x; v < nv; v += kThreads) P::put(d + E * v, P::gather(lds + shift + E * v));
+    for (int e = E * nv + threadIdx.x; e < n; e += kThreads) P::put1(d + e, lds[shift + e]);
     __syncthreads();
 }
 
 // One tile per workgroup (grid = number of tiles).
-template <typename OutT, bool kGeneral>
+template <typename SrcT, typename DstT, bool kGeneral>
 __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable t) {
-    constexpr int kTile = tile_elems<OutT>();
-    __shared__ __attribute__((aligned(16))) float lds[kGeneral ? kTile + 16 : 4];
+    constexpr int kTile = tile_elems<SrcT, DstT>();
+    __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral ? kTile + 16 : 8];
     const uint32_t tile = blockIdx.x;
     // wave-uniform lookup of the segment holding this tile
     uint32_t lo = 0, hi = t.nseg - 1;
@@ -248,16 +276,16 @@ __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable t) {
     const int64_t bn = (b + 1 == sg.nblk) ? sg.last_n : sg.blk_n;
     if (e0 >= bn) return;
     const int n = static_cast<int>(min(static_cast<int64_t>(kTile), bn - e0));
-    OutT* d = static_cast<OutT*>(sg.dst) + static_cast<int64_t>(b) * sg.dst_stride + e0;
+    DstT* d = static_cast<DstT*>(sg.dst) + static_cast<int64_t>(b) * sg.dst_stride + e0;
     if (sg.src == nullptr) {
-        tile_zero<OutT>(d, n);
+        tile_zero<SrcT, DstT>(d, n);
         return;
     }
-    const float* s = sg.src + static_cast<int64_t>(b) * sg.src_stride + e0;
+    const SrcT* s = static_cast<const SrcT*>(sg.src) + static_cast<int64_t>(b) * sg.src_stride + e0;
     if constexpr (kGeneral)
-        tile_general<OutT>(s, d, n, lds);
+        tile_general<SrcT, DstT>(s, d, n, lds);
     else
-        tile_aligned<OutT>(s, d, n);
+        tile_aligned<SrcT, DstT>(s, d, n);
 }
 
 // ---------------------------------------------------------------------------
@@ -269,9 +297,11 @@ struct ReduceArgs {
     const uint16_t* c[kMaxContrib];
     float* out;
     int64_t len;
-    int32_t nc;     // contributions in this launch
-    int32_t first;  // this launch holds rank 0's term: start from it
-    int32_t last;   // this launch applies the post divide
+    int32_t nc;          // contributions in this launch
+    int32_t group;       // hybrid: ranks per group (the launch holds whole groups)
+    int32_t first;       // the sum starts in this launch (else out holds the partial)
+    int32_t last;        // this launch divides by post (and accumulates)
+    int32_t unused0;     // (accumulation is a template parameter of the kernel)
     int32_t unused;
     float pre, rpre, post, unused2;
 };
@@ -288,6 +318,15 @@ __device__ __forceinline__ float term(uint32_t bits, const ReduceArgs& a) {
 }
 
 template <int kPre>
+__device__ __forceinline__ void set8(float* acc, u4 x, const ReduceArgs& a) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[2 * q] = term<kPre>(x[q] << 16, a);
+        acc[2 * q + 1] = term<kPre>(x[q] & 0xFFFF0000u, a);
+    }
+}
+
+template <int kPre>
 __device__ __forceinline__ void add8(float* acc, u4 x, const ReduceArgs& a) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -296,25 +335,57 @@ __device__ __forceinline__ void add8(float* acc, u4 x, const ReduceArgs& a) {
     }
 }
 
+// Adds ranks [r, end) to acc in rank order, loading kAhead ranks before their adds.
 template <int kPre>
-__device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
-    float acc;
-    int r = 0;
-    if (a.first) {
-        acc = term<kPre>(static_cast<uint32_t>(a.c[0][j]) << 16, a);
-        r = 1;
-    } else {
-        acc = a.out[j];
+__device__ __forceinline__ void add_ranks(float* acc, int r, int end, int64_t j0,
+                                          const ReduceArgs& a) {
+    constexpr int kAhead = FSDP_REDUCE_AHEAD;
+    for (; r + kAhead <= end; r += kAhead) {
+        u4 x[kAhead];
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) x[u] = ldu4(a.c[r + u] + j0);
+#pragma unroll
+        for (int u = 0; u < kAhead; ++u) add8<kPre>(acc, x[u], a);
     }
-    for (; r < a.nc; ++r) acc = acc + term<kPre>(static_cast<uint32_t>(a.c[r][j]) << 16, a);
-    if (a.last) acc = acc / a.post;
+    for (; r < end; ++r) add8<kPre>(acc, ldu4(a.c[r] + j0), a);
+}
+
+template <int kPre, bool kHybrid, bool kAccum>
+__device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
+    float acc = 0.0f;
+    if constexpr (!kHybrid) {
+        int r = 0;
+        if (a.first) {
+            acc = term<kPre>(static_cast<uint32_t>(a.c[0][j]) << 16, a);
+            r = 1;
+        } else {
+            acc = a.out[j];
+        }
+        for (; r < a.nc; ++r) acc = acc + term<kPre>(static_cast<uint32_t>(a.c[r][j]) << 16, a);
+    } else {
+        bool have = !a.first;
+        if (have) acc = a.out[j];
+        for (int g0 = 0; g0 < a.nc; g0 += a.group) {
+            float s = term<kPre>(static_cast<uint32_t>(a.c[g0][j]) << 16, a);
+            for (int r = g0 + 1; r < g0 + a.group; ++r)
+                s = s + term<kPre>(static_cast<uint32_t>(a.c[r][j]) << 16, a);
+            acc = have ? acc + s : s;
+            have = true;
+        }
+    }
+    if (a.last) {
+        acc = acc / a.post;
+        if constexpr (kAccum) acc = a.out[j] + acc;
+    }
     a.out[j] = acc;
 }
 
 // One tile of kReduceThreads * 8 outputs per workgroup.  Each lane owns 8
 // consecutive outputs; for every rank it loads their 8 bf16 as one 16-byte
-// vector, kAhead ranks at a time, then adds them strictly in rank order.
-template <int kPre, bool kVec>
+// vector (a wave reads 1 KiB contiguous per rank), kAhead ranks at a time, then
+// adds them strictly in rank order.  Hybrid: the same within each group of
+// ranks, then the group sums in group order.
+template <int kPre, bool kVec, bool kHybrid, bool kAccum>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
     constexpr int kEpt = 8;
     constexpr int kAhead = FSDP_REDUCE_AHEAD;
@@ -324,45 +395,123 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
         const int64_t j0 = blk * kPerBlk + static_cast<int64_t>(threadIdx.x) * kEpt;
         if (j0 + kEpt <= a.len) {
             float acc[kEpt];
-            int r = 0;
-            if (a.first) {
-                const u4 x = ldu4(a.c[0] + j0);
+            if constexpr (!kHybrid) {
+                int r = 0;
+                if (a.first) {
+                    set8<kPre>(acc, ldu4(a.c[0] + j0), a);
+                    r = 1;
+                } else {
+                    const f4 lo = ld4(a.out + j0), hi = ld4(a.out + j0 + 4);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = term<kPre>(x[q] << 16, a);
-                    acc[2 * q + 1] = term<kPre>(x[q] & 0xFFFF0000u, a);
+                    for (int q = 0; q < 4; ++q) {
+                        acc[q] = lo[q];
+                        acc[4 + q] = hi[q];
+                    }
                 }
-                r = 1;
+                add_ranks<kPre>(acc, r, a.nc, j0, a);
             } else {
-                const f4 lo = ld4(a.out + j0), hi = ld4(a.out + j0 + 4);
+                // Loads run kAhead ranks ahead regardless of group boundaries; a
+                // wave-uniform position-in-group counter starts each group's sum at its
+                // first rank and folds it into the total after its last.
+                bool have = !a.first;
+                if (have) {
+                    const f4 lo = ld4(a.out + j0), hi = ld4(a.out + j0 + 4);
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[q] = lo[q];
-                    acc[4 + q] = hi[q];
+                    for (int q = 0; q < 4; ++q) {
+                        acc[q] = lo[q];
+                        acc[4 + q] = hi[q];
+                    }
+                }
+                float s[kEpt];
+                int pos = 0;
+                for (int r = 0; r < a.nc; r += kAhead) {
+                    const int cnt = min(kAhead, a.nc - r);
+                    u4 x[kAhead];
+#pragma unroll
+                    for (int u = 0; u < kAhead; ++u)
+                        if (u < cnt) x[u] = ldu4(a.c[r + u] + j0);
+#pragma unroll
+                    for (int u = 0; u < kAhead; ++u) {
+                        if (u >= cnt) break;
+                        if (pos == 0) set8<kPre>(s, x[u], a); else add8<kPre>(s, x[u], a);
+                        if (++pos == a.group) {
+#pragma unroll
+                            for (int e = 0; e < kEpt; ++e) acc[e] = have ? acc[e] + s[e] : s[e];
+                            have = true;
+                            pos = 0;
+                        }
+                    }
                 }
             }
-            for (; r + kAhead <= a.nc; r += kAhead) {
-                u4 x[kAhead];
-#pragma unroll
-                for (int u = 0; u < kAhead; ++u) x[u] = ldu4(a.c[r + u] + j0);
-#pragma unroll
-                for (int u = 0; u < kAhead; ++u) add8<kPre>(acc, x[u], a);
-            }
-            for (; r < a.nc; ++r) add8<kPre>(acc, ldu4(a.c[r] + j0), a);
             if (a.last) {
 #pragma unroll
                 for (int e = 0; e < kEpt; ++e) acc[e] = acc[e] / a.post;
+                if constexpr (kAccum) {
+                    const f4 lo = *reinterpret_cast<const f4*>(a.out + j0);
+                    const f4 hi = *reinterpret_cast<const f4*>(a.out + j0 + 4);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[q] = lo[q] + acc[q];
+                        acc[4 + q] = hi[q] + acc[4 + q];
+                    }
+                }
             }
             st4(a.out + j0, f4{acc[0], acc[1], acc[2], acc[3]});
             st4(a.out + j0 + 4, f4{acc[4], acc[5], acc[6], acc[7]});
         } else {
-            for (int64_t j = j0; j < a.len && j < j0 + kEpt; ++j) reduce_one<kPre>(a, j);
+            for (int64_t j = j0; j < a.len && j < j0 + kEpt; ++j) reduce_one<kPre, kHybrid, kAccum>(a, j);
         }
     } else {
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) {
             const int64_t j = blk * kPerBlk + static_cast<int64_t>(e) * kReduceThreads + threadIdx.x;
-            if (j < a.len) reduce_one<kPre>(a, j);
+            if (j < a.len) reduce_one<kPre, kHybrid, kAccum>(a, j);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// local gradient accumulation (no communication): acc = (init ? 0 : acc) + fp32(g)
+// ---------------------------------------------------------------------------
+template <bool kInit, bool kVec>
+__global__ __launch_bounds__(kThreads) void accumulate_kernel(const uint16_t* __restrict__ g,
+                                                              float* __restrict__ acc,
+                                                              int64_t len) {
+    constexpr int64_t kPerBlk = static_cast<int64_t>(kThreads) * 8;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kPerBlk;
+    if (kVec && base + kPerBlk <= len) {
+        // lane l owns elements [4l, 4l+4) and [1024 + 4l, 1024 + 4l + 4) of the tile
+        u2 x[2];
+        f4 y[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t o = base + 4 * (threadIdx.x + h * kThreads);
+            x[h] = __builtin_nontemporal_load(reinterpret_cast<const u2*>(g + o));
+            if constexpr (!kInit) y[h] = ld4s<FSDP_ACC_NT != 0>(acc + o);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const f4 w = {__builtin_bit_cast(float, x[h][0] << 16),
+                          __builtin_bit_cast(float, x[h][0] & 0xFFFF0000u),
+                          __builtin_bit_cast(float, x[h][1] << 16),
+                          __builtin_bit_cast(float, x[h][1] & 0xFFFF0000u)};
+            f4 r;
+            if constexpr (kInit) {
+                r = w;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) r[q] = y[h][q] + w[q];
+            }
+            st4s<FSDP_ACC_NT != 0>(acc + base + 4 * (threadIdx.x + h * kThreads), r);
+        }
+        return;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int64_t j = base + static_cast<int64_t>(e) * kThreads + threadIdx.x;
+        if (j < len) {
+            const float w = __builtin_bit_cast(float, static_cast<uint32_t>(g[j]) << 16);
+            acc[j] = kInit ? w : acc[j] + w;
         }
     }
 }
@@ -454,10 +603,10 @@ bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 // Grid of `tiles` workgroups, one tile each (checked < 2^31 by the callers).
 dim3 grid_of(int64_t tiles) { return dim3(static_cast<unsigned>(std::max<int64_t>(1, tiles))); }
 
-template <typename OutT>
+template <typename SrcT, typename DstT>
 hipError_t launch_segcopy_t(const std::vector<CopySeg>& segs, hipStream_t stream) {
-    constexpr int64_t kTile = tile_elems<OutT>();
-    constexpr uintptr_t kDstAlign = Out<OutT>::kAlign;
+    constexpr int64_t kTile = tile_elems<SrcT, DstT>();
+    constexpr uintptr_t kDstAlign = Cp<SrcT, DstT>::kDstAlign;
     size_t i = 0;
     while (i < segs.size()) {
         SegTable t{};
@@ -483,35 +632,58 @@ hipError_t launch_segcopy_t(const std::vector<CopySeg>& segs, hipStream_t stream
             tiles += seg_tiles;
             // the vector path needs every block start aligned (tiles are multiples of 16 B)
             bool ok = aligned_to(c.dst, kDstAlign) &&
-                      (c.nblk == 1 || (c.dst_stride * sizeof(OutT)) % kDstAlign == 0);
+                      (c.nblk == 1 || (c.dst_stride * sizeof(DstT)) % kDstAlign == 0);
             if (c.src)
-                ok = ok && aligned_to(c.src, 16) && (c.nblk == 1 || (c.src_stride * 4) % 16 == 0);
+                ok = ok && aligned_to(c.src, 16) &&
+                     (c.nblk == 1 || (c.src_stride * sizeof(SrcT)) % 16 == 0);
             general = general || !ok;
         }
         if (t.nseg == 0) continue;
         t.ntiles = static_cast<uint32_t>(tiles);
         if (general)
-            hipLaunchKernelGGL((segcopy_kernel<OutT, true>), grid_of(tiles), dim3(kThreads), 0,
-                               stream, t);
+            hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, true>), grid_of(tiles), dim3(kThreads),
+                               0, stream, t);
         else
-            hipLaunchKernelGGL((segcopy_kernel<OutT, false>), grid_of(tiles), dim3(kThreads), 0,
-                               stream, t);
+            hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, false>), grid_of(tiles), dim3(kThreads),
+                               0, stream, t);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
 }
 
+template <int kPre, bool kVec>
+void launch_reduce_mode(const ReduceArgs& a, bool hybrid, bool accum, dim3 grid,
+                        hipStream_t stream) {
+    const dim3 block(kReduceThreads);
+    if (hybrid) {
+        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kVec, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((reduce_kernel<kPre, kVec, true, false>), grid, block, 0, stream, a);
+    } else {
+        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kVec, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((reduce_kernel<kPre, kVec, false, false>), grid, block, 0, stream, a);
+    }
+}
+
 }  // namespace
 
-hipError_t launch_segcopy(const std::vector<CopySeg>& segs, OutType out, hipStream_t stream) {
-    return out == OutType::kF32 ? launch_segcopy_t<float>(segs, stream)
-                                : launch_segcopy_t<uint16_t>(segs, stream);
+hipError_t launch_segcopy(const std::vector<CopySeg>& segs, Pipe pipe, hipStream_t stream) {
+    switch (pipe) {
+        case Pipe::kF32toF32: return launch_segcopy_t<float, float>(segs, stream);
+        case Pipe::kF32toBF16: return launch_segcopy_t<float, uint16_t>(segs, stream);
+        case Pipe::kBF16toBF16: return launch_segcopy_t<uint16_t, uint16_t>(segs, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib, int64_t len,
-                              float pre, float post, float* out, hipStream_t stream) {
+                              float pre, float post, int64_t group, bool accumulate, float* out,
+                              hipStream_t stream) {
     if (len <= 0 || n_contrib <= 0) return hipSuccess;
+    // one group of all ranks, or groups of one, are the flat sequential sum
+    const bool hybrid = group > 1 && group < n_contrib;
+    if (hybrid && (n_contrib % group != 0 || group > kMaxContrib)) return hipErrorInvalidValue;
+    if (accumulate && n_contrib > kMaxContrib) return hipErrorInvalidValue;
     int mode = kPreDiv;
     float rpre = 1.0f;
     if (pre == 1.0f) {
@@ -527,34 +699,54 @@ hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib
     const int64_t per_blk = static_cast<int64_t>(kReduceThreads) * 8;
     const int64_t blocks = (len + per_blk - 1) / per_blk;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    for (int64_t r0 = 0; r0 < n_contrib; r0 += kMaxContrib) {
+    // a launch holds up to kMaxContrib ranks; hybrid launches hold whole groups, so
+    // the running value carried in `out` between launches is always a complete sum
+    const int64_t chunk = hybrid ? (kMaxContrib / group) * group : kMaxContrib;
+    for (int64_t r0 = 0; r0 < n_contrib; r0 += chunk) {
         ReduceArgs a{};
-        a.nc = static_cast<int32_t>(std::min<int64_t>(kMaxContrib, n_contrib - r0));
+        a.nc = static_cast<int32_t>(std::min<int64_t>(chunk, n_contrib - r0));
         for (int32_t r = 0; r < a.nc; ++r) a.c[r] = contribs[r0 + r];
         a.out = out;
         a.len = len;
+        a.group = static_cast<int32_t>(hybrid ? group : a.nc);
         a.first = r0 == 0;
         a.last = r0 + a.nc == n_contrib;
         a.pre = pre;
         a.rpre = rpre;
         a.post = post;
-#define FSDP_LAUNCH_REDUCE(MODE)                                                              \
-    do {                                                                                      \
-        if (vec)                                                                              \
-            hipLaunchKernelGGL((reduce_kernel<MODE, true>), grid_of(blocks),                  \
-                               dim3(kReduceThreads), 0, stream, a);                           \
-        else                                                                                  \
-            hipLaunchKernelGGL((reduce_kernel<MODE, false>), grid_of(blocks),                 \
-                               dim3(kReduceThreads), 0, stream, a);                           \
-    } while (0)
-        if (mode == kPreNone) FSDP_LAUNCH_REDUCE(kPreNone);
-        else if (mode == kPreRecip) FSDP_LAUNCH_REDUCE(kPreRecip);
-        else FSDP_LAUNCH_REDUCE(kPreDiv);
-#undef FSDP_LAUNCH_REDUCE
+        const dim3 grid = grid_of(blocks);
+        if (mode == kPreNone) {
+            if (vec) launch_reduce_mode<kPreNone, true>(a, hybrid, accumulate, grid, stream);
+            else launch_reduce_mode<kPreNone, false>(a, hybrid, accumulate, grid, stream);
+        } else if (mode == kPreRecip) {
+            if (vec) launch_reduce_mode<kPreRecip, true>(a, hybrid, accumulate, grid, stream);
+            else launch_reduce_mode<kPreRecip, false>(a, hybrid, accumulate, grid, stream);
+        } else {
+            if (vec) launch_reduce_mode<kPreDiv, true>(a, hybrid, accumulate, grid, stream);
+            else launch_reduce_mode<kPreDiv, false>(a, hybrid, accumulate, grid, stream);
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+hipError_t launch_grad_accumulate(const uint16_t* grad, float* acc, int64_t len, bool init,
+                                  hipStream_t stream) {
+    if (len <= 0) return hipSuccess;
+    const int64_t per_blk = static_cast<int64_t>(kThreads) * 8;
+    const int64_t blocks = (len + per_blk - 1) / per_blk;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const bool vec = aligned_to(grad, 8) && aligned_to(acc, 16);
+    const dim3 grid = grid_of(blocks), block(kThreads);
+    if (init) {
+        if (vec) hipLaunchKernelGGL((accumulate_kernel<true, true>), grid, block, 0, stream, grad, acc, len);
+        else hipLaunchKernelGGL((accumulate_kernel<true, false>), grid, block, 0, stream, grad, acc, len);
+    } else {
+        if (vec) hipLaunchKernelGGL((accumulate_kernel<false, true>), grid, block, 0, stream, grad, acc, len);
+        else hipLaunchKernelGGL((accumulate_kernel<false, false>), grid, block, 0, stream, grad, acc, len);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* pb, int64_t len,

@@ -154,8 +154,17 @@ int plan_create(int32_t layout, int32_t n_params, const int32_t* ndims, const in
     return 0;
 }
 
-void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, float* out,
-                  std::vector<CopySeg>* segs) {
+namespace {
+const void* at(const void* p, int64_t e, size_t esize) {
+    return static_cast<const char*>(p) + e * static_cast<int64_t>(esize);
+}
+void* at(void* p, int64_t e, size_t esize) {
+    return static_cast<char*>(p) + e * static_cast<int64_t>(esize);
+}
+}  // namespace
+
+void plan_flatten(const UnitPlan& u, const void* const* params, int64_t k, void* out,
+                  size_t esize, std::vector<CopySeg>* segs) {
     segs->clear();
     if (u.layout == kFlat) {
         const int64_t base = k < 0 ? 0 : k * u.S;
@@ -166,8 +175,8 @@ void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, floa
             const int64_t hi = std::min(p.offset + p.numel, base + len);
             if (lo >= hi) continue;
             CopySeg s;
-            s.src = params[i] + (lo - p.offset);
-            s.dst = out + (lo - base);
+            s.src = at(params[i], lo - p.offset, esize);
+            s.dst = at(out, lo - base, esize);
             s.blk_n = s.last_n = hi - lo;
             s.nblk = 1;
             segs->push_back(s);
@@ -175,7 +184,7 @@ void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, floa
         const int64_t zlo = std::max(u.T, base);
         if (zlo < base + len) {
             CopySeg s;
-            s.dst = out + (zlo - base);
+            s.dst = at(out, zlo - base, esize);
             s.blk_n = s.last_n = base + len - zlo;
             s.nblk = 1;
             segs->push_back(s);
@@ -193,13 +202,13 @@ void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, floa
         // ranks whose chunk is complete (c rows), the one short rank, then empty ranks
         const int64_t n_full = p.rows / c;
         const int64_t short_rows = p.rows - n_full * c;
-        float* base = out + p.offset;
+        void* base = at(out, p.offset, esize);
         {  // full ranks in [k0, k1)
             const int64_t a = k0, b = std::min(k1, n_full);
             if (a < b) {
                 CopySeg s;
-                s.src = params[i] + a * seg_n;
-                s.dst = base + (a - k0) * u.S;
+                s.src = at(params[i], a * seg_n, esize);
+                s.dst = at(base, (a - k0) * u.S, esize);
                 s.blk_n = s.last_n = seg_n;
                 s.src_stride = seg_n;
                 s.dst_stride = u.S;
@@ -213,13 +222,13 @@ void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, floa
             const int64_t ks = n_full;
             if (ks >= k0 && ks < k1) {
                 CopySeg s;
-                s.src = params[i] + ks * seg_n;
-                s.dst = base + (ks - k0) * u.S;
+                s.src = at(params[i], ks * seg_n, esize);
+                s.dst = at(base, (ks - k0) * u.S, esize);
                 s.blk_n = s.last_n = short_rows * r;
                 s.nblk = 1;
                 segs->push_back(s);
                 CopySeg z;
-                z.dst = base + (ks - k0) * u.S + short_rows * r;
+                z.dst = at(base, (ks - k0) * u.S + short_rows * r, esize);
                 z.blk_n = z.last_n = (c - short_rows) * r;
                 z.nblk = 1;
                 segs->push_back(z);
@@ -229,7 +238,7 @@ void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, floa
             const int64_t a = std::max(k0, first_empty), b = k1;
             if (a < b) {
                 CopySeg z;
-                z.dst = base + (a - k0) * u.S;
+                z.dst = at(base, (a - k0) * u.S, esize);
                 z.blk_n = z.last_n = seg_n;
                 z.dst_stride = u.S;
                 z.nblk = b - a;
@@ -239,15 +248,15 @@ void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, floa
     }
 }
 
-void plan_copyout(const UnitPlan& u, const float* gathered, uint16_t* const* outs,
-                  std::vector<CopySeg>* segs) {
+void plan_copyout(const UnitPlan& u, const void* gathered, size_t src_esize, void* const* outs,
+                  size_t dst_esize, std::vector<CopySeg>* segs) {
     segs->clear();
     for (size_t i = 0; i < u.params.size(); ++i) {
         const ParamPlan& p = u.params[i];
         if (p.numel == 0) continue;
         if (u.layout == kFlat) {
             CopySeg s;
-            s.src = gathered + p.offset;
+            s.src = at(gathered, p.offset, src_esize);
             s.dst = outs[i];
             s.blk_n = s.last_n = p.numel;
             s.nblk = 1;
@@ -260,7 +269,7 @@ void plan_copyout(const UnitPlan& u, const float* gathered, uint16_t* const* out
         const int64_t short_rows = p.rows - n_full * c;
         if (n_full > 0) {
             CopySeg s;
-            s.src = gathered + p.offset;
+            s.src = at(gathered, p.offset, src_esize);
             s.dst = outs[i];
             s.blk_n = s.last_n = seg_n;
             s.src_stride = u.S;
@@ -270,13 +279,26 @@ void plan_copyout(const UnitPlan& u, const float* gathered, uint16_t* const* out
         }
         if (short_rows > 0) {
             CopySeg s;
-            s.src = gathered + n_full * u.S + p.offset;
-            s.dst = outs[i] + n_full * seg_n;
+            s.src = at(gathered, n_full * u.S + p.offset, src_esize);
+            s.dst = at(outs[i], n_full * seg_n, dst_esize);
             s.blk_n = s.last_n = short_rows * r;
             s.nblk = 1;
             segs->push_back(s);
         }
     }
+}
+
+void plan_whole(const UnitPlan& u, int64_t k, const void* src, void* dst,
+                std::vector<CopySeg>* segs) {
+    segs->clear();
+    const int64_t n = k < 0 ? u.L : u.S;
+    if (n == 0) return;
+    CopySeg s;
+    s.src = src;
+    s.dst = dst;
+    s.blk_n = s.last_n = n;
+    s.nblk = 1;
+    segs->push_back(s);
 }
 
 }  // namespace fsdp

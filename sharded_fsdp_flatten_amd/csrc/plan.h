@@ -44,9 +44,9 @@ int plan_create(int32_t layout, int32_t n_params, const int32_t* ndims, const in
 // One planned movement: `nblk` blocks; block b moves `blk_n` elements (the last
 // block `last_n`) from src + b*src_stride to dst + b*dst_stride.  src == nullptr
 // means "write zeros".  Strides and counts are in elements of the respective
-// buffer (fp32 for src; fp32 or bf16 for dst).
+// buffer (fp32 or bf16 for either side; the element sizes are the caller's).
 struct CopySeg {
-    const float* src = nullptr;
+    const void* src = nullptr;
     void* dst = nullptr;
     int64_t blk_n = 0;
     int64_t last_n = 0;
@@ -56,13 +56,18 @@ struct CopySeg {
 };
 
 // Segments that write rank k's shard (k = -1: every rank, gathered layout) into
-// `out` from the parameters.
-void plan_flatten(const UnitPlan& u, const float* const* params, int64_t k, float* out,
-                  std::vector<CopySeg>* segs);
+// `out` from the parameters; `esize` is the element size in bytes of both.
+void plan_flatten(const UnitPlan& u, const void* const* params, int64_t k, void* out,
+                  size_t esize, std::vector<CopySeg>* segs);
 
-// Segments that copy the gathered buffer out into per-parameter tensors
-// (dst elements are bf16).
-void plan_copyout(const UnitPlan& u, const float* gathered, uint16_t* const* outs,
-                  std::vector<CopySeg>* segs);
+// Segments that copy the gathered buffer (elements of `src_esize` bytes) out
+// into per-parameter tensors (elements of `dst_esize` bytes).
+void plan_copyout(const UnitPlan& u, const void* gathered, size_t src_esize, void* const* outs,
+                  size_t dst_esize, std::vector<CopySeg>* segs);
+
+// One segment covering rank k's shard (k = -1: the whole gathered buffer):
+// src and dst index the same positions.
+void plan_whole(const UnitPlan& u, int64_t k, const void* src, void* dst,
+                std::vector<CopySeg>* segs);
 
 }  // namespace fsdp

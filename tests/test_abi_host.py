@@ -284,3 +284,77 @@ def test_last_error_is_per_call(B):
     assert B.fsdp_last_error() == ""
     assert B.fsdp_status_string(3) == "FSDP_E_ALIGN"
     assert B.fsdp_status_string(99) == "FSDP_E_UNKNOWN"
+
+
+# ---------------------------------------------------------------------------
+# next rows: cast before gather, bf16 copy-out / copy-in, hybrid and accumulating
+# reduction, local accumulation
+# ---------------------------------------------------------------------------
+
+def test_reduce_ex_errors(B):
+    lib = B.load()
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(64,)], 8)
+    good = [FAKE] * 8
+    for group in (3, 5, 7, 9, -1):
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_grad_reduce_shard_ex(u, good, 1.0, 1.0, FAKE, group=group, stream=0)
+        assert _status(e) == "FSDP_E_RANGE", group
+    for pre, post in [(0.0, 1.0), (1.0, float("inf"))]:
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_grad_reduce_shard_ex(u, good, pre, post, FAKE, group=2, stream=0)
+        assert _status(e) == "FSDP_E_RANGE"
+    assert lib.fsdp_grad_reduce_shard_ex(u.handle, None, None, FAKE, None) == 1  # opts NULL
+    big = B.fsdp_unit_create(B.FSDP_FLAT, [(512 * 4,)], 512)
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_grad_reduce_shard_ex(big, [FAKE] * 512, 1.0, 1.0, FAKE, group=256, stream=0)
+    assert _status(e) == "FSDP_E_UNSUPPORTED"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_grad_reduce_shard_ex(big, [FAKE] * 512, 1.0, 1.0, FAKE, accumulate=True, stream=0)
+    assert _status(e) == "FSDP_E_UNSUPPORTED"
+    with pytest.raises(B.FsdpError) as e:
+        B.fsdp_grad_reduce_shard_ex(u, [FAKE] * 7 + [FAKE + 1], 1.0, 1.0, FAKE, group=4, stream=0)
+    assert _status(e) == "FSDP_E_ALIGN"
+
+
+def test_cast_copyin_accumulate_errors(B):
+    u = B.fsdp_unit_create(B.FSDP_ROWS, [(5, 3), (4,)], 4)
+    for k in (4, -2):
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_cast_to_bf16(u, k, FAKE, FAKE, stream=0)
+        assert _status(e) == "FSDP_E_RANGE"
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_flatten_shard_bf16(u, [FAKE, FAKE], k, FAKE, stream=0)
+        assert _status(e) == "FSDP_E_RANGE"
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_grad_accumulate(u, k, FAKE, FAKE, True, stream=0)
+        assert _status(e) == "FSDP_E_RANGE"
+    cases = [
+        (lambda: B.fsdp_cast_to_bf16(u, 0, 0, FAKE, stream=0), "FSDP_E_ARG"),
+        (lambda: B.fsdp_cast_to_bf16(u, 0, FAKE + 2, FAKE, stream=0), "FSDP_E_ALIGN"),
+        (lambda: B.fsdp_cast_to_bf16(u, B.FSDP_ALL_RANKS, FAKE, FAKE + 1, stream=0), "FSDP_E_ALIGN"),
+        (lambda: B.fsdp_unflatten_copyout_bf16(u, 0, [FAKE, FAKE], stream=0), "FSDP_E_ARG"),
+        (lambda: B.fsdp_unflatten_copyout_bf16(u, FAKE, [FAKE, FAKE + 1], stream=0), "FSDP_E_ALIGN"),
+        (lambda: B.fsdp_unflatten_copyout_bf16(u, FAKE + 1, [FAKE, FAKE], stream=0), "FSDP_E_ALIGN"),
+        (lambda: B.fsdp_flatten_shard_bf16(u, [FAKE, 0], 0, FAKE, stream=0), "FSDP_E_ARG"),
+        (lambda: B.fsdp_flatten_shard_bf16(u, [FAKE, FAKE], 0, 0, stream=0), "FSDP_E_ARG"),
+        (lambda: B.fsdp_flatten_shard_bf16(u, [FAKE + 1, FAKE], 0, FAKE, stream=0), "FSDP_E_ALIGN"),
+        (lambda: B.fsdp_grad_accumulate(u, 0, 0, FAKE, False, stream=0), "FSDP_E_ARG"),
+        (lambda: B.fsdp_grad_accumulate(u, 0, FAKE, FAKE + 2, False, stream=0), "FSDP_E_ALIGN"),
+    ]
+    for fn, want in cases:
+        with pytest.raises(B.FsdpError) as e:
+            fn()
+        assert _status(e) == want
+
+
+def test_next_rows_noops_on_empty_units(B):
+    for layout in (B.FSDP_FLAT, B.FSDP_ROWS):
+        for shapes in ([], [(0,)], [(0, 5), (3, 0)]):
+            u = B.fsdp_unit_create(layout, shapes, 4)
+            B.fsdp_cast_to_bf16(u, 0, 0, 0, stream=0)
+            B.fsdp_cast_to_bf16(u, B.FSDP_ALL_RANKS, 0, 0, stream=0)
+            B.fsdp_unflatten_copyout_bf16(u, 0, [0] * len(shapes), stream=0)
+            B.fsdp_flatten_shard_bf16(u, [0] * len(shapes), B.FSDP_ALL_RANKS, 0, stream=0)
+            B.fsdp_grad_reduce_shard_ex(u, [0] * 4, 1.0, 1.0, 0, group=2, accumulate=True, stream=0)
+            B.fsdp_grad_accumulate(u, B.FSDP_ALL_RANKS, 0, 0, True, stream=0)
+            assert B.fsdp_last_error() == ""
