@@ -1,0 +1,44 @@
+"""bench.py keeps its output contract: one JSON line with the required keys, consistent
+per-kernel numbers, the roofline object of the dominant kernel and the CPU baseline."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+from conftest import ROOT
+
+pytestmark = pytest.mark.gpu
+
+REQUIRED = ["metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+            "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config", "kernels",
+            "roofline", "cpu_baseline"]
+
+
+def _run(*args, timeout=240):
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], cwd=ROOT,
+                       stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, timeout=timeout)
+    return p
+
+
+def test_bench_json_line_on_the_tiny_unit():
+    p = _run("--workload", "tiny", "--steps", "5", "--warmup", "1", "--next")
+    assert p.returncode == 0, p.stderr[-2000:]
+    lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    for k in REQUIRED:
+        assert k in d, k
+    assert d["n_gpus"] == 1 and d["steps"] == 5 and d["warmup"] == 1
+    assert d["unit"] == "GB/s" and d["higher_is_better"] is True and d["data"] == "synthetic"
+    assert set(d["kernels"]) == {"grad_reduce", "copyout", "adamw", "flatten"}
+    step_bytes = sum(k["bytes"] for k in d["kernels"].values())
+    assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"] + 0.1
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["sample"]
+    assert "copyin_bf16_all_ranks" in d["next_rows"]
+
