@@ -23,8 +23,10 @@
 //   - grad_reduce: each lane owns 8 consecutive outputs, loads 8 bf16 of 8
 //     ranks at a time (128-bit each) before adding them in rank order.
 //   - adamw: elementwise over 8 elements per lane, 128-bit loads and stores.
-//     Its state is read and written back in place, and here the plain cache
-//     policy measures faster than the non-temporal one (6.5 vs 5.6 TB/s).
+//     Its state is read and written back in place: plain loads measure faster
+//     than nt ones (6.5 vs 5.6 TB/s), and nt stores put its writes in HBM within
+//     its own launch (plain stores leave them dirty in the 256 MB Infinity Cache,
+//     which costs the next kernels, or AdamW itself once they outgrow it).
 // Every floating-point step is one IEEE binary32 operation, in the order the
 // CPU oracle fixes; contraction into FMA is disabled for this file.
 #include <hip/hip_runtime.h>
@@ -71,8 +73,11 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #ifndef FSDP_ADAM_THREADS
 #define FSDP_ADAM_THREADS 256
 #endif
-#ifndef FSDP_ADAM_NT
-#define FSDP_ADAM_NT 0      // p, m, v are read and written back in place: plain accesses
+#ifndef FSDP_ADAM_NT_LOAD
+#define FSDP_ADAM_NT_LOAD 0   // AdamW reads p, g, m, v with plain loads
+#endif
+#ifndef FSDP_ADAM_NT_STORE
+#define FSDP_ADAM_NT_STORE 1  // and streams p, m, v back with nt stores
 #endif
 
 constexpr int kThreads = FSDP_COPY_THREADS;
@@ -551,7 +556,8 @@ __device__ __forceinline__ void adam_one(const AdamArgs& a, int64_t j) {
 // l + kAdamThreads (4 elements each) of every array.
 template <bool kVec, bool kBf16>
 __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
-    constexpr bool kNT = FSDP_ADAM_NT != 0;
+    constexpr bool kNTL = FSDP_ADAM_NT_LOAD != 0;
+    constexpr bool kNTS = FSDP_ADAM_NT_STORE != 0;
     constexpr int64_t kPerBlk = static_cast<int64_t>(kAdamThreads) * 8;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kPerBlk;
     if constexpr (kVec) {
@@ -560,10 +566,10 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int64_t o = base + 4 * (threadIdx.x + h * kAdamThreads);
-                p[h] = ld4s<kNT>(a.p + o);
-                g[h] = ld4s<kNT>(a.g + o);
-                m[h] = ld4s<kNT>(a.m + o);
-                v[h] = ld4s<kNT>(a.v + o);
+                p[h] = ld4s<kNTL>(a.p + o);
+                g[h] = ld4s<kNTL>(a.g + o);
+                m[h] = ld4s<kNTL>(a.m + o);
+                v[h] = ld4s<kNTL>(a.v + o);
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -579,9 +585,9 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int64_t o = base + 4 * (threadIdx.x + h * kAdamThreads);
-                st4s<kNT>(a.p + o, p[h]);
-                st4s<kNT>(a.m + o, m[h]);
-                st4s<kNT>(a.v + o, v[h]);
+                st4s<kNTS>(a.p + o, p[h]);
+                st4s<kNTS>(a.m + o, m[h]);
+                st4s<kNTS>(a.v + o, v[h]);
                 if constexpr (kBf16)
                     stu2(a.pb + o, u2{pack_bf16x2(p[h][0], p[h][1]), pack_bf16x2(p[h][2], p[h][3])});
             }

@@ -432,6 +432,33 @@ def test_t5_block_full_size():
         assert_bf16_bits(to_host(o), w, "t5 copy-out %d" % i)
 
 
+def test_t5_block_full_size_reduce_and_adamw():
+    """T5-11B block shard (S = 25,165,952), N = 8: the reduction of 8 bf16 contributions and
+    two AdamW steps, every element against the oracle."""
+    unit = W.t5_11b_block(N=8)
+    u = B.fsdp_unit_create(B.FSDP_FLAT, unit.shapes, unit.N)
+    S = u.S
+    c = W.device_contribs(unit.N, S, step=1)
+    grad = torch.empty(S, device=dev())
+    B.fsdp_grad_reduce_shard(u, [c[r] for r in range(unit.N)], 2.0, 4.0, grad)
+    _sync()
+    g_host = oracle.grad_reduce(list(to_host(c)), 2.0, 4.0)
+    assert_f32_tol_then_bits(to_host(grad), g_host, "t5 reduce")
+    del c
+    hp = unit.adam
+    gen = torch.Generator(device=dev()).manual_seed(3)
+    p = torch.randn(S, device=dev(), generator=gen).mul_(unit.std)
+    m, v = torch.zeros(S, device=dev()), torch.zeros(S, device=dev())
+    hp_, hm, hv = to_host(p).copy(), np.zeros(S, np.float32), np.zeros(S, np.float32)
+    for t in (1, 2):
+        B.fsdp_adam_shard(u, p, grad, m, v, step=t, **hp)
+        oracle.adamw(hp_, g_host, hm, hv, step=t, **hp)
+        _sync()
+        assert_f32_tol_then_bits(to_host(p), hp_, "t5 adam p t=%d" % t)
+        assert_f32_tol_then_bits(to_host(m), hm, "t5 adam m t=%d" % t)
+        assert_f32_tol_then_bits(to_host(v), hv, "t5 adam v t=%d" % t)
+
+
 @pytest.fixture(scope="module")
 def big175():
     unit = W.gpt175b_block(N=128)
