@@ -84,6 +84,7 @@ constexpr int kThreads = FSDP_COPY_THREADS;
 constexpr int kMaxSegs = 48;           // segments per launch (kernel-argument budget)
 constexpr int kMaxContrib = 128;       // contribution pointers per reduce launch
 constexpr int kReduceThreads = FSDP_REDUCE_THREADS;
+static_assert(kReduceThreads % 64 == 0, "reduce workgroups are whole wave64s (lane exchange)");
 constexpr int kAdamThreads = FSDP_ADAM_THREADS;
 
 // ---------------------------------------------------------------------------
@@ -461,8 +462,29 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
                     }
                 }
             }
-            st4(a.out + j0, f4{acc[0], acc[1], acc[2], acc[3]});
-            st4(a.out + j0 + 4, f4{acc[4], acc[5], acc[6], acc[7]});
+            if (blk * kPerBlk + kPerBlk <= a.len) {
+                // Whole tile in the vector path: swap halves across lanes (ds_bpermute,
+                // no LDS allocation) so that each store instruction writes 1 KiB of
+                // whole cache lines; lane l stores outputs 4l..4l+3 of each 256-output
+                // half of its wave's 512, which lane 32h + l/2 holds.
+                const int lane = threadIdx.x & 63;
+                float* wave_out = a.out + blk * kPerBlk + (threadIdx.x & ~63) * kEpt;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const int src = 32 * h + (lane >> 1);
+                    float w[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float lo = __shfl(acc[i], src, 64);
+                        const float hi = __shfl(acc[4 + i], src, 64);
+                        w[i] = (lane & 1) ? hi : lo;
+                    }
+                    st4(wave_out + 256 * h + 4 * lane, f4{w[0], w[1], w[2], w[3]});
+                }
+            } else {
+                st4(a.out + j0, f4{acc[0], acc[1], acc[2], acc[3]});
+                st4(a.out + j0 + 4, f4{acc[4], acc[5], acc[6], acc[7]});
+            }
         } else {
             for (int64_t j = j0; j < a.len && j < j0 + kEpt; ++j) reduce_one<kPre, kHybrid, kAccum>(a, j);
         }
