@@ -45,6 +45,8 @@ def parse_args():
     ap.add_argument("--workload", default="gpt175b",
                     choices=["gpt175b", "t5", "gpt2l", "rows", "tiny"])
     ap.add_argument("--rank", type=int, default=None, help="rank k (default: N/2 - 1)")
+    ap.add_argument("--ranks", type=int, default=None,
+                    help="shard the unit over this many ranks instead of its own N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--contribs", default="stacked", choices=["stacked", "separate"],
                     help="gradient contributions as one [N, S] receive buffer (default) or as "
@@ -76,10 +78,11 @@ def load_traffic(per_launch_bytes_expected):
     return t.get("copyout_hbm_bytes_per_launch")
 
 
-def make_unit(name):
+def make_unit(name, ranks=None):
     import workloads as W
-    return {"gpt175b": W.gpt175b_block, "t5": W.t5_11b_block, "gpt2l": W.gpt2_large_block,
-            "rows": W.gpt2_large_emb_rows, "tiny": W.tiny_mlp}[name]()
+    make = {"gpt175b": W.gpt175b_block, "t5": W.t5_11b_block, "gpt2l": W.gpt2_large_block,
+            "rows": W.gpt2_large_emb_rows, "tiny": W.tiny_mlp}[name]
+    return make() if ranks is None else make(N=ranks)
 
 
 def pre_post(N):
@@ -219,7 +222,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    unit = make_unit(args.workload)
+    unit = make_unit(args.workload, args.ranks)
     N = unit.N
     k = args.rank if args.rank is not None else max(0, N // 2 - 1)
     layout = B.FSDP_FLAT if unit.layout == W.FLAT else B.FSDP_ROWS

@@ -341,42 +341,114 @@ __device__ __forceinline__ void add8(float* acc, u4 x, const ReduceArgs& a) {
     }
 }
 
+// How the vector path reads a rank's 8 bf16 (the output is 16-byte aligned unless
+// kLdScalar): kLdWord, every contribution at least 4-byte aligned: one four-dword
+// load (global loads of several dwords need dword alignment only).  kLdHalf, some
+// contribution only 2-byte aligned: such a rank's 8 elements are read as the four
+// dwords that start one element early plus the dword after them, then shifted by
+// one element.
+enum : int { kLdScalar = 0, kLdWord = 1, kLdHalf = 2 };
+
+typedef uint32_t u4w __attribute__((ext_vector_type(4), aligned(4)));
+
+__device__ __forceinline__ u4 ldw4(const uint16_t* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u4w*>(p));
+}
+
+// Rank r's elements j0 .. j0+7 (j0 a multiple of 8, all inside the rank's buffer),
+// read in two steps so that a batch of ranks issues all its loads before any shift.
+// kLdHalf: o = 1 when the buffer is only 2-byte aligned, else 0; the lane reads four
+// dwords from element j0 - o on and one at element j0 + 6 + o (j0 + 7 and j0 + 8 when
+// o = 1; when o = 0 two of the lane's own, unused).  Each dword read holds at least
+// one of the lane's 8 elements, so no read reaches a page the buffer does not.
+struct Raw {
+    u4 v;
+    uint32_t w4;
+};
+
+__device__ __forceinline__ int half_off(const uint16_t* c) {
+    return static_cast<int>(reinterpret_cast<uintptr_t>(c) >> 1) & 1;
+}
+
+template <int kLd>
+__device__ __forceinline__ Raw load_raw(const ReduceArgs& a, int r, int64_t j0) {
+    Raw x;
+    if constexpr (kLd == kLdWord) {
+        x.v = ldw4(a.c[r] + j0);
+    } else {
+        const int o = half_off(a.c[r]);
+        const uint16_t* p = a.c[r] + j0 - o;  // dword aligned
+        x.v = ldw4(p);
+        x.w4 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p + 6 + 2 * o));
+    }
+    return x;
+}
+
+template <int kLd>
+__device__ __forceinline__ u4 finish(const Raw& x, const ReduceArgs& a, int r) {
+    if constexpr (kLd == kLdWord) {
+        return x.v;
+    } else {
+        const uint32_t b = 2u * static_cast<uint32_t>(half_off(a.c[r]));  // bytes
+        const uint32_t w[5] = {x.v[0], x.v[1], x.v[2], x.v[3], x.w4};
+        u4 y;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) y[q] = __builtin_amdgcn_alignbyte(w[q + 1], w[q], b);
+        return y;
+    }
+}
+
+template <int kLd>
+__device__ __forceinline__ u4 load_c(const ReduceArgs& a, int r, int64_t j0) {
+    return finish<kLd>(load_raw<kLd>(a, r, j0), a, r);
+}
+
 // Adds ranks [r, end) to acc in rank order, loading kAhead ranks before their adds.
-template <int kPre>
+template <int kPre, int kLd>
 __device__ __forceinline__ void add_ranks(float* acc, int r, int end, int64_t j0,
                                           const ReduceArgs& a) {
     constexpr int kAhead = FSDP_REDUCE_AHEAD;
     for (; r + kAhead <= end; r += kAhead) {
-        u4 x[kAhead];
+        Raw x[kAhead];
 #pragma unroll
-        for (int u = 0; u < kAhead; ++u) x[u] = ldu4(a.c[r + u] + j0);
+        for (int u = 0; u < kAhead; ++u) x[u] = load_raw<kLd>(a, r + u, j0);
 #pragma unroll
-        for (int u = 0; u < kAhead; ++u) add8<kPre>(acc, x[u], a);
+        for (int u = 0; u < kAhead; ++u) add8<kPre>(acc, finish<kLd>(x[u], a, r + u), a);
     }
-    for (; r < end; ++r) add8<kPre>(acc, ldu4(a.c[r] + j0), a);
+    for (; r < end; ++r) add8<kPre>(acc, load_c<kLd>(a, r, j0), a);
 }
 
+// One output, for buffers that are not 16-byte aligned and for the ragged last tile.
+// Up to 8 ranks are loaded before their adds, which run in the vector path's order.
 template <int kPre, bool kHybrid, bool kAccum>
 __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
-    float acc = 0.0f;
-    if constexpr (!kHybrid) {
-        int r = 0;
-        if (a.first) {
-            acc = term<kPre>(static_cast<uint32_t>(a.c[0][j]) << 16, a);
-            r = 1;
-        } else {
-            acc = a.out[j];
-        }
-        for (; r < a.nc; ++r) acc = acc + term<kPre>(static_cast<uint32_t>(a.c[r][j]) << 16, a);
-    } else {
-        bool have = !a.first;
-        if (have) acc = a.out[j];
-        for (int g0 = 0; g0 < a.nc; g0 += a.group) {
-            float s = term<kPre>(static_cast<uint32_t>(a.c[g0][j]) << 16, a);
-            for (int r = g0 + 1; r < g0 + a.group; ++r)
-                s = s + term<kPre>(static_cast<uint32_t>(a.c[r][j]) << 16, a);
-            acc = have ? acc + s : s;
-            have = true;
+    constexpr int kBatch = 8;
+    bool have = !a.first;
+    float acc = have ? a.out[j] : 0.0f;
+    float s = 0.0f;
+    int pos = 0;
+    for (int r = 0; r < a.nc; r += kBatch) {
+        const int cnt = min(kBatch, a.nc - r);
+        float t[kBatch];
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u)
+            if (u < cnt) t[u] = term<kPre>(static_cast<uint32_t>(a.c[r + u][j]) << 16, a);
+#pragma unroll
+        for (int u = 0; u < kBatch; ++u) {
+            if (u >= cnt) break;
+            if constexpr (!kHybrid) {
+                // one running sum in rank order, continuing the previous launch's
+                acc = have ? acc + t[u] : t[u];
+                have = true;
+            } else {
+                // group sums, each folded into the total after the group's last rank
+                s = pos == 0 ? t[u] : s + t[u];
+                if (++pos == a.group) {
+                    acc = have ? acc + s : s;
+                    have = true;
+                    pos = 0;
+                }
+            }
         }
     }
     if (a.last) {
@@ -390,21 +462,22 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
 // consecutive outputs; for every rank it loads their 8 bf16 as one 16-byte
 // vector (a wave reads 1 KiB contiguous per rank), kAhead ranks at a time, then
 // adds them strictly in rank order.  Hybrid: the same within each group of
-// ranks, then the group sums in group order.
-template <int kPre, bool kVec, bool kHybrid, bool kAccum>
+// ranks, then the group sums in group order.  kLd: how contributions are read
+// (the output is 16-byte aligned unless kLd is kLdScalar).
+template <int kPre, int kLd, bool kHybrid, bool kAccum>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
     constexpr int kEpt = 8;
     constexpr int kAhead = FSDP_REDUCE_AHEAD;
     constexpr int64_t kPerBlk = static_cast<int64_t>(kReduceThreads) * kEpt;
     const int64_t blk = blockIdx.x;
-    if constexpr (kVec) {
+    if constexpr (kLd != kLdScalar) {
         const int64_t j0 = blk * kPerBlk + static_cast<int64_t>(threadIdx.x) * kEpt;
         if (j0 + kEpt <= a.len) {
             float acc[kEpt];
             if constexpr (!kHybrid) {
                 int r = 0;
                 if (a.first) {
-                    set8<kPre>(acc, ldu4(a.c[0] + j0), a);
+                    set8<kPre>(acc, load_c<kLd>(a, 0, j0), a);
                     r = 1;
                 } else {
                     const f4 lo = ld4(a.out + j0), hi = ld4(a.out + j0 + 4);
@@ -414,7 +487,7 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
                         acc[4 + q] = hi[q];
                     }
                 }
-                add_ranks<kPre>(acc, r, a.nc, j0, a);
+                add_ranks<kPre, kLd>(acc, r, a.nc, j0, a);
             } else {
                 // Loads run kAhead ranks ahead regardless of group boundaries; a
                 // wave-uniform position-in-group counter starts each group's sum at its
@@ -432,14 +505,15 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
                 int pos = 0;
                 for (int r = 0; r < a.nc; r += kAhead) {
                     const int cnt = min(kAhead, a.nc - r);
-                    u4 x[kAhead];
+                    Raw x[kAhead];
 #pragma unroll
                     for (int u = 0; u < kAhead; ++u)
-                        if (u < cnt) x[u] = ldu4(a.c[r + u] + j0);
+                        if (u < cnt) x[u] = load_raw<kLd>(a, r + u, j0);
 #pragma unroll
                     for (int u = 0; u < kAhead; ++u) {
                         if (u >= cnt) break;
-                        if (pos == 0) set8<kPre>(s, x[u], a); else add8<kPre>(s, x[u], a);
+                        const u4 v = finish<kLd>(x[u], a, r + u);
+                        if (pos == 0) set8<kPre>(s, v, a); else add8<kPre>(s, v, a);
                         if (++pos == a.group) {
 #pragma unroll
                             for (int e = 0; e < kEpt; ++e) acc[e] = have ? acc[e] + s[e] : s[e];
@@ -680,16 +754,16 @@ hipError_t launch_segcopy_t(const std::vector<CopySeg>& segs, hipStream_t stream
     return hipSuccess;
 }
 
-template <int kPre, bool kVec>
+template <int kPre, int kLd>
 void launch_reduce_mode(const ReduceArgs& a, bool hybrid, bool accum, dim3 grid,
                         hipStream_t stream) {
     const dim3 block(kReduceThreads);
     if (hybrid) {
-        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kVec, true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((reduce_kernel<kPre, kVec, true, false>), grid, block, 0, stream, a);
+        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kLd, true, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((reduce_kernel<kPre, kLd, true, false>), grid, block, 0, stream, a);
     } else {
-        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kVec, false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((reduce_kernel<kPre, kVec, false, false>), grid, block, 0, stream, a);
+        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kLd, false, true>), grid, block, 0, stream, a);
+        else hipLaunchKernelGGL((reduce_kernel<kPre, kLd, false, false>), grid, block, 0, stream, a);
     }
 }
 
@@ -722,8 +796,11 @@ hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib
         rpre = 1.0f / pre;
         if (mant == 0.5f && std::isnormal(rpre) && rpre * pre == 1.0f) mode = kPreRecip;
     }
-    bool vec = aligned_to(out, 16);
-    for (int64_t r = 0; r < n_contrib; ++r) vec = vec && aligned_to(contribs[r], 16);
+    // vector path when the output is 16-byte aligned; contributions only 2-byte
+    // aligned are read one element early and shifted
+    bool all4 = true;
+    for (int64_t r = 0; r < n_contrib; ++r) all4 = all4 && aligned_to(contribs[r], 4);
+    const int ld = !aligned_to(out, 16) ? kLdScalar : all4 ? kLdWord : kLdHalf;
     const int64_t per_blk = static_cast<int64_t>(kReduceThreads) * 8;
     const int64_t blocks = (len + per_blk - 1) / per_blk;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
@@ -744,14 +821,17 @@ hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib
         a.post = post;
         const dim3 grid = grid_of(blocks);
         if (mode == kPreNone) {
-            if (vec) launch_reduce_mode<kPreNone, true>(a, hybrid, accumulate, grid, stream);
-            else launch_reduce_mode<kPreNone, false>(a, hybrid, accumulate, grid, stream);
+            if (ld == kLdWord) launch_reduce_mode<kPreNone, kLdWord>(a, hybrid, accumulate, grid, stream);
+            else if (ld == kLdHalf) launch_reduce_mode<kPreNone, kLdHalf>(a, hybrid, accumulate, grid, stream);
+            else launch_reduce_mode<kPreNone, kLdScalar>(a, hybrid, accumulate, grid, stream);
         } else if (mode == kPreRecip) {
-            if (vec) launch_reduce_mode<kPreRecip, true>(a, hybrid, accumulate, grid, stream);
-            else launch_reduce_mode<kPreRecip, false>(a, hybrid, accumulate, grid, stream);
+            if (ld == kLdWord) launch_reduce_mode<kPreRecip, kLdWord>(a, hybrid, accumulate, grid, stream);
+            else if (ld == kLdHalf) launch_reduce_mode<kPreRecip, kLdHalf>(a, hybrid, accumulate, grid, stream);
+            else launch_reduce_mode<kPreRecip, kLdScalar>(a, hybrid, accumulate, grid, stream);
         } else {
-            if (vec) launch_reduce_mode<kPreDiv, true>(a, hybrid, accumulate, grid, stream);
-            else launch_reduce_mode<kPreDiv, false>(a, hybrid, accumulate, grid, stream);
+            if (ld == kLdWord) launch_reduce_mode<kPreDiv, kLdWord>(a, hybrid, accumulate, grid, stream);
+            else if (ld == kLdHalf) launch_reduce_mode<kPreDiv, kLdHalf>(a, hybrid, accumulate, grid, stream);
+            else launch_reduce_mode<kPreDiv, kLdScalar>(a, hybrid, accumulate, grid, stream);
         }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -245,6 +245,32 @@ def test_hybrid_and_accumulate_misaligned_scalar_path():
     assert_f32_tol_then_bits(to_host(out), want, "misaligned hybrid accumulate")
 
 
+@pytest.mark.parametrize("N,group,accumulate", [(16, 4, True), (12, 3, False), (256, 32, False),
+                                                (8, 0, True)])
+def test_hybrid_and_accumulate_realigned_contribs(N, group, accumulate):
+    """Aligned output, contributions at 2-byte offsets 1..7: the shifted-granule vector
+    path under hybrid groups, accumulation and chained launches."""
+    rng = np.random.Generator(np.random.PCG64(65 + N))
+    S = 6007
+    c = W.host_contribs(N, S, step=5)
+    views, keep = [], []
+    for r in range(N):
+        v, base = offset_view(S, torch.bfloat16, int(rng.integers(1, 8)))
+        v.copy_(to_dev(c[r]))
+        views.append(v)
+        keep.append(base)
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    old = W.host_normal(S, 1e-3, seed=9)
+    out = to_dev(old) if accumulate else torch.full((S,), float("nan"), device=dev())
+    assert out.data_ptr() % 16 == 0
+    B.fsdp_grad_reduce_shard_ex(u, views, 2.0, N / 2.0, out, group=group, accumulate=accumulate)
+    _sync()
+    want = old.copy() if accumulate else None
+    got_want = oracle.grad_reduce_ex(list(c), 2.0, N / 2.0, group=group, out=want)
+    assert_f32_tol_then_bits(to_host(out), want if accumulate else got_want,
+                             "realigned hybrid N=%d group=%d acc=%d" % (N, group, accumulate))
+
+
 # ---------------------------------------------------------------------------
 # local accumulation without communication (NEXT-3)
 # ---------------------------------------------------------------------------

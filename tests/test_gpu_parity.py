@@ -324,6 +324,47 @@ def test_grad_reduce_misaligned_and_special_values():
                                  "misaligned pre=%g post=%g" % (pre, post))
 
 
+@pytest.mark.parametrize("N,S,pre,post,seed", [
+    (9, 5003, 2.0, 4.5, 11), (128, 4101, 8.0, 16.0, 12), (130, 2051, 1.0, 130.0, 13),
+    (3, 517, 3.0, 1.0, 14), (16, 100003, 4.0, 4.0, 15), (8, 7, 2.0, 4.0, 16)])
+def test_grad_reduce_realigned_contribs(N, S, pre, post, seed):
+    """Output 16-byte aligned, each contribution at a 2-byte offset of its own (rank 0
+    misaligned, the others drawn from 0..7): the vector path reads the two aligned
+    granules around a lane's 8 elements and shifts them into place."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = W.host_contribs(N, S, step=seed)
+    offs = rng.integers(0, 8, size=N)
+    offs[0] = 5
+    views, keep = [], []
+    for r in range(N):
+        v, base = offset_view(S, torch.bfloat16, int(offs[r]))
+        v.copy_(to_dev(c[r]))
+        views.append(v)
+        keep.append(base)
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    out = torch.full((S,), float("nan"), device=dev())
+    assert out.data_ptr() % 16 == 0
+    B.fsdp_grad_reduce_shard(u, views, pre, post, out)
+    _sync()
+    assert_f32_tol_then_bits(to_host(out), oracle.grad_reduce(list(c), pre, post),
+                             "realigned N=%d S=%d" % (N, S))
+
+
+@pytest.mark.parametrize("N,S", [(120, 3001), (16, 8197), (7, 1030), (129, 1027), (130, 2050)])
+def test_grad_reduce_stacked_rows_off_16_bytes(N, S):
+    """Rows of one [N, S] receive buffer with S % 8 != 0 start at every 2-byte offset."""
+    c = W.host_contribs(N, S, step=21)
+    buf = to_dev(c)
+    rows = [buf[r] for r in range(N)]
+    assert len({r.data_ptr() % 16 for r in rows}) > 1
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    out = torch.full((S,), float("nan"), device=dev())
+    B.fsdp_grad_reduce_shard(u, rows, 4.0, N / 4.0, out)
+    _sync()
+    assert_f32_tol_then_bits(to_host(out), oracle.grad_reduce(list(c), 4.0, N / 4.0),
+                             "stacked N=%d S=%d" % (N, S))
+
+
 # ---------------------------------------------------------------------------
 # AdamW
 # ---------------------------------------------------------------------------
@@ -541,3 +582,20 @@ def test_gpt175b_padded_n120_flatten(big175):
         B.fsdp_flatten_shard(u, d_params, k, out)
         _sync()
         assert_f32_bits(to_host(out), oracle.flat_shard(params, 120, k), "175b N=120 k=%d" % k)
+
+
+def test_gpt175b_n120_grad_reduce_full(big175):
+    """N = 120 on the GPT-175B block: S = 15,100,826, so the rows of the [120, S] receive
+    buffer start 0, 4, 8 or 12 bytes past a 16-byte boundary."""
+    unit, _ = big175
+    u = B.fsdp_unit_create(B.FSDP_FLAT, unit.shapes, 120)
+    assert u.S == 15_100_826
+    c = W.device_contribs(120, u.S, step=4)
+    assert {c[r].data_ptr() % 16 for r in range(120)} == {0, 4, 8, 12}
+    out = torch.empty(u.S, device=dev())
+    B.fsdp_grad_reduce_shard(u, [c[r] for r in range(120)], 8.0, 15.0, out)
+    _sync()
+    c_host = to_host(c)
+    del c
+    assert_f32_tol_then_bits(to_host(out), oracle.grad_reduce(list(c_host), 8.0, 15.0),
+                             "175b N=120 reduce")
