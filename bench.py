@@ -54,6 +54,15 @@ def parse_args():
     ap.add_argument("--next", action="store_true",
                     help="also time the next rows (hybrid + accumulating reduce, bf16 copy-in, "
                          "cast, bf16 copy-out, local accumulation) in a second cold-cache loop")
+    ap.add_argument("--flush", default="auto", choices=["auto", "on", "off"],
+                    help="read 1 GiB before every timed kernel so that nothing it reads can sit in "
+                         "the 256 MB Infinity Cache (auto: on when the copy-out moves < 2 GB, where "
+                         "the step order alone does not guarantee it); with flushing, the step time "
+                         "is the sum of the kernels' event times")
+    ap.add_argument("--sweep-ranks", action="store_true",
+                    help="also time flatten, reduce and AdamW for every rank (N <= 8) or for ranks "
+                         "0, 1, N/2-1, N-1, each launch after a 1 GiB read flush; reports the worst "
+                         "rank")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 4 GiB fp32 copy through the library (N = 1 unit) "
                          "and hipMemcpy device-to-device, as copy ceilings")
@@ -76,6 +85,15 @@ def load_traffic(per_launch_bytes_expected):
     if t.get("kernel_src_sha256") != kernel_src_hash():
         return None
     return t.get("copyout_hbm_bytes_per_launch")
+
+
+def time_stats(ms):
+    """Mean, median, min and p90 of a list of kernel times (ms)."""
+    srt = sorted(ms)
+    n = len(srt)
+    med = srt[n // 2] if n % 2 else 0.5 * (srt[n // 2 - 1] + srt[n // 2])
+    p90 = srt[min(n - 1, max(0, -(-9 * n // 10) - 1))]
+    return sum(ms) / n, med, srt[0], p90
 
 
 def make_unit(name, ranks=None):
@@ -152,7 +170,7 @@ def cpu_baseline(host, unit, N, k, S, valid, pre, post, hp, rows):
 
 
 def time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows, grad, outs,
-                   gathered, adam_p, stream):
+                   gathered, adam_p, stream, flush=None):
     """The next rows, in an order where no kernel reads what the previous one just wrote:
     hybrid reduction (groups of 8 ranks) accumulating into the grad shard; copy-in of
     per-parameter bf16 gradients into the ReduceScatter input (all ranks); cast of rank k's
@@ -182,6 +200,8 @@ def time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows, gra
     reps = max(5, args.steps // 5)
     for _ in range(reps):
         for n in order:
+            if flush is not None:
+                flush()
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -199,6 +219,49 @@ def time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows, gra
                   "elements_per_s": float("%.4g" % (elems / (ms * 1e-3))), "reps": reps}
     out["hybrid_group"] = group
     del rs_input, shard16
+    return out
+
+
+def sweep_ranks(B, u, N, contrib_rows, pre, post, hp, params, grad, shard, adam_p, m, v,
+                stream, flush, reps=10):
+    """Flatten, reduce and AdamW for each swept rank k, each launch after a 1 GiB read flush.
+    Reduce and AdamW move the same bytes for every rank (the shard length is the same);
+    flatten reads only rank k's real elements."""
+    import torch
+    ks = list(range(N)) if N <= 8 else sorted({0, 1, max(0, N // 2 - 1), N - 1})
+    out = {"ranks": ks, "reps": reps}
+    worst = {}
+    for k in ks:
+        info = u.info(k)
+        S, valid = info["S"], info["valid"]
+        kern = {
+            "grad_reduce": (lambda: B.fsdp_grad_reduce_shard(u, contrib_rows, pre, post, grad),
+                            (2 * N + 4) * S),
+            "adamw": (lambda: B.fsdp_adam_shard(u, adam_p, grad, m, v, step=2, **hp), 28 * S),
+            "flatten": (lambda k=k: B.fsdp_flatten_shard(u, params, k, shard), 4 * valid + 4 * S),
+        }
+        row = {}
+        for name, (fn, nbytes) in kern.items():
+            fn()
+            ev = []
+            for _ in range(reps):
+                flush()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev.append((e0, e1))
+            torch.cuda.synchronize()
+            _, med, _, p90 = time_stats([a.elapsed_time(b) for a, b in ev])
+            gbs = nbytes / (med * 1e-3) / 1e9
+            row[name] = {"ms_median": round(med, 4), "ms_p90": round(p90, 4),
+                         "GB/s": round(gbs, 1), "bytes": nbytes}
+            if name not in worst or gbs < worst[name]["GB/s"]:
+                worst[name] = {"rank": k, "GB/s": round(gbs, 1),
+                               "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        out[str(k)] = row
+    out["worst"] = worst
     return out
 
 
@@ -250,6 +313,16 @@ def main():
     v = torch.zeros(S, device=dev)
     torch.cuda.synchronize()
 
+    flush_on = args.flush == "on" or (args.flush == "auto" and 6 * T < 2e9)
+    # The flush READS 1 GiB: that evicts what the cache held and leaves it clean.  Writing
+    # 1 GiB instead would leave it full of dirty lines whose write-back the next kernel
+    # would pay for (AdamW measured 53% of peak after such a flush, 82% in the step).
+    flush_buf = torch.zeros(1 << 28, device=dev)
+    flush_sum = torch.zeros((), device=dev)
+
+    def flush():
+        torch.sum(flush_buf, dim=0, out=flush_sum)
+
     bytes_k = {
         "grad_reduce": (2 * N + 4) * S,
         "copyout": 6 * T,
@@ -274,6 +347,8 @@ def main():
 
     def step(events=None):
         for name in order:
+            if flush_on:
+                flush()
             if events is not None:
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -294,15 +369,19 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    ms_k = {n: sum(a.elapsed_time(b) for a, b in events[n]) / args.steps for n in order}
-    ms_step = wall * 1e3 / args.steps
+    times = {n: [a.elapsed_time(b) for a, b in events[n]] for n in order}
+    ms_k = {n: sum(times[n]) / args.steps for n in order}
+    # with flushing the fills sit between the kernels, so the step is the kernels' sum
+    ms_step = sum(ms_k.values()) if flush_on else wall * 1e3 / args.steps
     step_bytes = sum(bytes_k.values())
     kernels = {}
     for n in order:
         gbs = bytes_k[n] / (ms_k[n] * 1e-3) / 1e9
+        _, med, lo, p90 = time_stats(times[n])
         kernels[n] = {"ms": round(ms_k[n], 4), "bytes": bytes_k[n], "GB/s": round(gbs, 1),
                       "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
-                      "elements_per_s": float("%.4g" % (elems_k[n] / (ms_k[n] * 1e-3)))}
+                      "elements_per_s": float("%.4g" % (elems_k[n] / (ms_k[n] * 1e-3))),
+                      "ms_median": round(med, 4), "ms_min": round(lo, 4), "ms_p90": round(p90, 4)}
     kernels["grad_reduce"]["input_elements_per_s"] = float(
         "%.4g" % (N * S / (ms_k["grad_reduce"] * 1e-3)))
 
@@ -327,7 +406,9 @@ def main():
                                                   "FSDP1 flat" if layout == B.FSDP_FLAT
                                                   else "FSDP2 dim-0 row", N, k),
                    "N": N, "rank": k, "S": S, "T": T, "pre_divide": pre, "post_divide": post,
-                   "contribs": args.contribs},
+                   "contribs": args.contribs,
+                   "step_time": ("sum of the kernels' event times, 1 GiB read before each kernel"
+                                 if flush_on else "wall clock")},
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -336,7 +417,13 @@ def main():
 
     if args.next:
         result["next_rows"] = time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows,
-                                             grad, outs, gathered, adam_p, stream)
+                                             grad, outs, gathered, adam_p, stream,
+                                             flush if flush_on else None)
+
+    if args.sweep_ranks:
+        result["per_rank"] = sweep_ranks(B, u, N, contrib_rows, pre, post, hp, params, grad, shard,
+                                         adam_p, m, v, stream, flush)
+    del flush_buf
 
     if args.copy_probe:
         n = 1 << 30

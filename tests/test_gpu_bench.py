@@ -23,7 +23,7 @@ def _run(*args, timeout=240):
 
 
 def test_bench_json_line_on_the_tiny_unit():
-    p = _run("--workload", "tiny", "--steps", "5", "--warmup", "1", "--next")
+    p = _run("--workload", "tiny", "--steps", "5", "--warmup", "1", "--next", "--sweep-ranks")
     assert p.returncode == 0, p.stderr[-2000:]
     lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
     assert len(lines) == 1
@@ -35,6 +35,16 @@ def test_bench_json_line_on_the_tiny_unit():
     assert set(d["kernels"]) == {"grad_reduce", "copyout", "adamw", "flatten"}
     step_bytes = sum(k["bytes"] for k in d["kernels"].values())
     assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"] + 0.1
+    # the tiny unit fits the Infinity Cache: kernels run after a flush, the step is their sum
+    assert d["config"]["step_time"].startswith("sum of the kernels")
+    assert abs(d["ms_per_step"] - sum(k["ms"] for k in d["kernels"].values())) < 1e-3
+    for k in d["kernels"].values():
+        assert k["ms_min"] <= k["ms_median"] <= k["ms_p90"]
+    pr = d["per_rank"]
+    assert pr["ranks"] == [0, 1, 2, 3]
+    for k in pr["ranks"]:
+        assert set(pr[str(k)]) == {"grad_reduce", "adamw", "flatten"}
+    assert set(pr["worst"]) == {"grad_reduce", "adamw", "flatten"}
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
