@@ -12,7 +12,9 @@ and every byte counted comes from HBM.  Inputs are synthetic (seeded normals in
 the unit's shapes) and already resident in HBM when the timed region starts.
 
 Default workload: GPT-175B style block unit (d = 12288, 1,812,099,072 fp32
-elements), FSDP1 flat sharding over N = 128, rank 63.
+elements), FSDP1 flat sharding over N = 128, rank 63; the 128 contributions sit
+in one receive buffer with rows at the library's recommended pitch (S rounded
+up to whole 128-byte lines).
 
 Prints one JSON line (metric, value in GB/s over the whole step, per-kernel
 GB/s, fraction of the 8 TB/s HBM peak and elements/s, the roofline of the
@@ -48,9 +50,10 @@ def parse_args():
     ap.add_argument("--ranks", type=int, default=None,
                     help="shard the unit over this many ranks instead of its own N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--contribs", default="stacked", choices=["stacked", "separate"],
-                    help="gradient contributions as one [N, S] receive buffer (default) or as "
-                         "N separate allocations")
+    ap.add_argument("--contribs", default="pitched", choices=["pitched", "stacked", "separate"],
+                    help="gradient contributions as one receive buffer with rows at the library's "
+                         "recommended pitch (S rounded up to whole 128-byte lines; default), as one "
+                         "[N, S] buffer with rows S apart, or as N separate allocations")
     ap.add_argument("--next", action="store_true",
                     help="also time the next rows (hybrid + accumulating reduce, bf16 copy-in, "
                          "cast, bf16 copy-out, local accumulation) in a second cold-cache loop")
@@ -300,11 +303,12 @@ def main():
     gen = torch.Generator(device=dev).manual_seed(12345)
     gathered = torch.randn(L, device=dev, generator=gen).mul_(unit.std)
     outs = [torch.empty(s, dtype=torch.bfloat16, device=dev) for s in unit.shapes]
-    contribs = W.device_contribs(N, S, step=1)
-    if args.contribs == "stacked":
-        contrib_rows = [contribs[r] for r in range(N)]
-    else:
+    pitch = u.recv_pitch if args.contribs == "pitched" else S
+    contribs = W.device_contribs(N, S, step=1, pitch=pitch)
+    if args.contribs == "separate":
         contrib_rows = [contribs[r].clone() for r in range(N)]
+    else:
+        contrib_rows = [contribs[r] for r in range(N)]
     grad = torch.zeros(S, device=dev)  # written by the reduction, read by AdamW
     shard = torch.empty(S, device=dev)
     adam_p = torch.empty(S, device=dev)
@@ -406,7 +410,8 @@ def main():
                                                   "FSDP1 flat" if layout == B.FSDP_FLAT
                                                   else "FSDP2 dim-0 row", N, k),
                    "N": N, "rank": k, "S": S, "T": T, "pre_divide": pre, "post_divide": post,
-                   "contribs": args.contribs,
+                   "contribs": args.contribs if args.contribs == "separate"
+                   else "%s (one buffer, row pitch %d elements)" % (args.contribs, pitch),
                    "step_time": ("sum of the kernels' event times, 1 GiB read before each kernel"
                                  if flush_on else "wall clock")},
         "kernels": kernels,

@@ -162,6 +162,16 @@ FSDP_API fsdp_status fsdp_unit_info(const fsdp_unit* unit, int32_t k, fsdp_unit_
  * rank's ROWS segment (the q_i of FSDP_ROWS). */
 FSDP_API fsdp_status fsdp_unit_param_offset(const fsdp_unit* unit, int32_t i, int64_t* offset);
 
+/* Recommended row pitch, in elements, of a stacked [N][pitch] bf16 buffer that
+ * receives the N gradient contributions of fsdp_grad_reduce_shard (row r holds
+ * contribution r in its first S elements): S rounded up to a whole 128-byte
+ * line (a multiple of 64 elements).  The reduction reads each contribution in
+ * 1 KiB runs; rows that start mid-line make every run of theirs touch one more
+ * line (at N = 128 on the GPT-175B block, 6.25% more HBM reads and a 6% slower
+ * reduction than line-aligned rows).  Any layout works; this one is fastest.
+ * Host only.  Errors: FSDP_E_ARG (null unit or pitch). */
+FSDP_API fsdp_status fsdp_unit_recv_pitch(const fsdp_unit* unit, int64_t* pitch);
+
 /*
  * Shard a unit ([P1] section 3.4, FlatParameter, Fig. 3; [P2] section 2).
  *   params : host array of n_params device pointers, parameter i holding

@@ -26,5 +26,6 @@ from .binding import (  # noqa: F401
     fsdp_unit_destroy,
     fsdp_unit_info,
     fsdp_unit_param_offset,
+    fsdp_unit_recv_pitch,
     load,
 )

@@ -83,6 +83,8 @@ def load() -> ctypes.CDLL:
     lib.fsdp_unit_info.restype = st
     lib.fsdp_unit_param_offset.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
     lib.fsdp_unit_param_offset.restype = st
+    lib.fsdp_unit_recv_pitch.argtypes = [_vp, ctypes.POINTER(ctypes.c_int64)]
+    lib.fsdp_unit_recv_pitch.restype = st
     lib.fsdp_flatten_shard.argtypes = [_vp, _vp, ctypes.c_int32, _vp, _vp]
     lib.fsdp_flatten_shard.restype = st
     lib.fsdp_unflatten_copyout.argtypes = [_vp, _vp, _vp, _vp]
@@ -210,6 +212,11 @@ class Unit:
     def offset(self, i: int) -> int:
         return fsdp_unit_param_offset(self, i)
 
+    @property
+    def recv_pitch(self) -> int:
+        """Recommended row pitch (elements) of a stacked [N, pitch] bf16 receive buffer."""
+        return fsdp_unit_recv_pitch(self)
+
 
 def fsdp_unit_create(layout: int, shapes: Sequence[Sequence[int]], N: int) -> Unit:
     lib = load()
@@ -238,6 +245,12 @@ def fsdp_unit_param_offset(unit: Unit, i: int) -> int:
     off = ctypes.c_int64()
     _check(load().fsdp_unit_param_offset(unit.handle, i, ctypes.byref(off)))
     return int(off.value)
+
+
+def fsdp_unit_recv_pitch(unit: Unit) -> int:
+    pitch = ctypes.c_int64()
+    _check(load().fsdp_unit_recv_pitch(unit.handle, ctypes.byref(pitch)))
+    return int(pitch.value)
 
 
 def fsdp_flatten_shard(unit: Unit, params: Sequence, k: int, shard, stream=None) -> None:
@@ -359,7 +372,7 @@ def fsdp_grad_accumulate(unit: Unit, k: int, grad, acc, init: bool, stream=None)
 
 
 ABI_FUNCTIONS = ["fsdp_abi_version", "fsdp_last_error", "fsdp_status_string", "fsdp_unit_create",
-                 "fsdp_unit_destroy", "fsdp_unit_info", "fsdp_unit_param_offset",
+                 "fsdp_unit_destroy", "fsdp_unit_info", "fsdp_unit_param_offset", "fsdp_unit_recv_pitch",
                  "fsdp_flatten_shard", "fsdp_unflatten_copyout", "fsdp_grad_reduce_shard",
                  "fsdp_adam_shard", "fsdp_cast_to_bf16", "fsdp_unflatten_copyout_bf16",
                  "fsdp_flatten_shard_bf16", "fsdp_grad_reduce_shard_ex", "fsdp_grad_accumulate"]

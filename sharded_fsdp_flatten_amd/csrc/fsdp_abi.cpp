@@ -191,6 +191,15 @@ fsdp_status fsdp_unit_param_offset(const fsdp_unit* unit, int32_t i, int64_t* of
     return ok();
 }
 
+fsdp_status fsdp_unit_recv_pitch(const fsdp_unit* unit, int64_t* pitch) {
+    if (!unit || !pitch) return fail(FSDP_E_ARG, "unit and pitch must not be NULL");
+    constexpr int64_t kLine = 64;  // bf16 elements per 128-byte line
+    const int64_t S = unit->plan.S;
+    // S <= L fits int64 with room for the round-up (plan_create bounds L)
+    *pitch = (S + kLine - 1) / kLine * kLine;
+    return ok();
+}
+
 fsdp_status fsdp_flatten_shard(const fsdp_unit* unit, const float* const* params, int32_t k,
                                float* shard, void* stream) {
     if (!unit) return fail(FSDP_E_ARG, "unit is NULL");

@@ -186,6 +186,26 @@ def test_info_and_offset_errors(B):
         u.offset(2)
 
 
+def test_recv_pitch(B):
+    """S rounded up to whole 128-byte lines (64 bf16), for both layouts; null arguments fail."""
+    import ctypes
+    cases = [(B.FSDP_FLAT, [(W.gpt175b_block().shapes[0])], 128),
+             (B.FSDP_FLAT, W.gpt175b_block().shapes, 128), (B.FSDP_FLAT, W.gpt175b_block().shapes, 120),
+             (B.FSDP_FLAT, [(64 * 5,)], 5), (B.FSDP_FLAT, [(65,)], 1), (B.FSDP_FLAT, [(3,)], 4),
+             (B.FSDP_ROWS, W.gpt2_large_emb_rows().shapes, 8), (B.FSDP_FLAT, [], 3)]
+    for layout, shapes, N in cases:
+        u = B.fsdp_unit_create(layout, shapes, N)
+        p = u.recv_pitch
+        assert p % 64 == 0 and u.S <= p < u.S + 64, (u.S, p)
+    assert B.fsdp_unit_create(B.FSDP_FLAT, W.gpt175b_block().shapes, 128).recv_pitch == 14_157_056
+    assert B.fsdp_unit_create(B.FSDP_FLAT, [(64 * 5,)], 5).recv_pitch == 64
+    assert B.fsdp_unit_create(B.FSDP_FLAT, [], 3).recv_pitch == 0
+    lib = B.load()
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(4,)], 2)
+    assert lib.fsdp_unit_recv_pitch(u.handle, None) == 1
+    assert lib.fsdp_unit_recv_pitch(None, ctypes.byref(ctypes.c_int64())) == 1
+
+
 def test_flatten_errors(B):
     u = B.fsdp_unit_create(B.FSDP_FLAT, [(4,), (3,)], 2)
     cases = [

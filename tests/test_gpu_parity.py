@@ -538,8 +538,12 @@ def test_gpt175b_copyout_full(big175):
 
 
 def test_gpt175b_grad_reduce_full(big175):
+    """The benchmarked configuration: 128 contributions in one receive buffer whose rows sit
+    at the recommended pitch (S rounded up to whole 128-byte lines)."""
     unit, u = big175
-    c = W.device_contribs(unit.N, u.S, step=1)
+    assert u.recv_pitch == 14_157_056
+    c = W.device_contribs(unit.N, u.S, step=1, pitch=u.recv_pitch)
+    assert all(c[r].data_ptr() % 128 == c[0].data_ptr() % 128 for r in range(unit.N))
     out = torch.empty(u.S, device=dev())
     B.fsdp_grad_reduce_shard(u, [c[r] for r in range(unit.N)], 8.0, 16.0, out)
     _sync()

@@ -165,10 +165,16 @@ def device_params(unit: Unit, seed: int = 0, device: str = "cuda"):
     return out
 
 
-def device_contribs(N: int, length: int, std: float = 1e-3, step: int = 1, device: str = "cuda"):
-    """[N, length] bf16 contributions drawn on the device (one row per rank)."""
+def device_contribs(N: int, length: int, std: float = 1e-3, step: int = 1, device: str = "cuda",
+                    pitch: int = None):
+    """[N, length] bf16 contributions drawn on the device (one row per rank).  With `pitch`
+    the rows sit `pitch` elements apart in one buffer and the [N, length] view is returned."""
     import torch
-    out = torch.empty((N, length), dtype=torch.bfloat16, device=device)
+    pitch = length if pitch is None else pitch
+    if pitch < length:
+        raise ValueError("pitch must be at least the row length")
+    buf = torch.empty((N, pitch), dtype=torch.bfloat16, device=device)
+    out = buf[:, :length]
     g = torch.Generator(device=device)
     for r in range(N):
         g.manual_seed(contrib_seed(step, r))
