@@ -102,6 +102,16 @@ __device__ __forceinline__ f4 ld4(const float* p) {
 __device__ __forceinline__ u4 ldu4(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u4*>(p));
 }
+// 16-byte loads from addresses that are only 4-byte aligned (global loads of
+// several dwords need dword alignment only); they read exactly those 16 bytes.
+typedef float f4w __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u4w __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ f4 ld4w(const float* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const f4w*>(p));
+}
+__device__ __forceinline__ u4 ldu4w(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u4w*>(p));
+}
 __device__ __forceinline__ void st4(float* p, f4 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<f4*>(p));
 }
@@ -143,6 +153,7 @@ template <> struct Cp<float, float> {
     static constexpr unsigned kDstAlign = 16;  // bytes a vector store needs
     using V = f4;
     __device__ static V load(const float* p) { return ld4(p); }
+    __device__ static V loadw(const float* p) { return ld4w(p); }
     __device__ static V gather(const float* p) { return f4{p[0], p[1], p[2], p[3]}; }
     __device__ static void put(float* d, V x) { st4(d, x); }
     __device__ static void put1(float* d, float x) { *d = x; }
@@ -154,6 +165,7 @@ template <> struct Cp<float, uint16_t> {
     static constexpr unsigned kDstAlign = 8;
     using V = f4;
     __device__ static V load(const float* p) { return ld4(p); }
+    __device__ static V loadw(const float* p) { return ld4w(p); }
     __device__ static V gather(const float* p) { return f4{p[0], p[1], p[2], p[3]}; }
     __device__ static void put(uint16_t* d, V x) {
         stu2(d, u2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
@@ -167,6 +179,7 @@ template <> struct Cp<uint16_t, uint16_t> {
     static constexpr unsigned kDstAlign = 16;
     using V = u4;
     __device__ static V load(const uint16_t* p) { return ldu4(p); }
+    __device__ static V loadw(const uint16_t* p) { return ldu4w(p); }
     __device__ static V gather(const uint16_t* p) {
         return u4{p[0] | (uint32_t{p[1]} << 16), p[2] | (uint32_t{p[3]} << 16),
                   p[4] | (uint32_t{p[5]} << 16), p[6] | (uint32_t{p[7]} << 16)};
@@ -195,22 +208,24 @@ struct SegTable {
 };
 static_assert(sizeof(SegTable) <= 4096, "segment table must fit one kernel argument block");
 
-// n <= tile elements; s 16-byte aligned, d aligned for its vector store.
-template <typename SrcT, typename DstT>
+// n <= tile elements; s 16-byte aligned (kWord: 4-byte aligned), d aligned for its
+// vector store.
+template <typename SrcT, typename DstT, bool kWord = false>
 __device__ __forceinline__ void tile_aligned(const SrcT* __restrict__ s, DstT* __restrict__ d,
                                              int n) {
     using P = Cp<SrcT, DstT>;
     constexpr int E = P::E, kVpl = P::kVpl;
+    const auto load = [](const SrcT* p) { return kWord ? P::loadw(p) : P::load(p); };
     const int nv = n / E;
     if (nv == kThreads * kVpl) {  // full tile: all loads issued before any store
         typename P::V x[kVpl];
 #pragma unroll
-        for (int u = 0; u < kVpl; ++u) x[u] = P::load(s + E * (threadIdx.x + u * kThreads));
+        for (int u = 0; u < kVpl; ++u) x[u] = load(s + E * (threadIdx.x + u * kThreads));
 #pragma unroll
         for (int u = 0; u < kVpl; ++u) P::put(d + E * (threadIdx.x + u * kThreads), x[u]);
         return;
     }
-    for (int v = threadIdx.x; v < nv; v += kThreads) P::put(d + E * v, P::load(s + E * v));
+    for (int v = threadIdx.x; v < nv; v += kThreads) P::put(d + E * v, load(s + E * v));
     for (int e = E * nv + threadIdx.x; e < n; e += kThreads) P::put1(d + e, s[e]);
 }
 
@@ -236,10 +251,11 @@ __device__ __forceinline__ void tile_zero(DstT* d, int n) {
 }
 
 // Any element-aligned source and destination.  A short head of scalar stores
-// aligns the destination; if the source is then off a 16-byte boundary by
-// `shift` elements, the tile is loaded as aligned 16-byte vectors (covering
-// exactly the 16-byte blocks that hold the tile, so no access leaves them) into
-// LDS and re-read at the shift.  Tile-uniform control flow (barriers).
+// aligns the destination.  A source then 4-byte aligned (always, for fp32) is read
+// with 16-byte loads at its own address.  A bf16 source at an odd element offset is
+// loaded as aligned 16-byte vectors (covering exactly the 16-byte blocks that hold
+// the tile, so no access leaves them) into LDS and re-read at the shift; that path
+// has tile-uniform control flow (barriers).
 template <typename SrcT, typename DstT>
 __device__ __forceinline__ void tile_general(const SrcT* s, DstT* d, int n, SrcT* lds) {
     using P = Cp<SrcT, DstT>;
@@ -252,6 +268,10 @@ __device__ __forceinline__ void tile_general(const SrcT* s, DstT* d, int n, SrcT
     const int shift = static_cast<int>((reinterpret_cast<uintptr_t>(s) & 15u) / sizeof(SrcT));
     if (shift == 0) {
         tile_aligned<SrcT, DstT>(s, d, n);
+        return;
+    }
+    if (sizeof(SrcT) >= 4 || (shift & 1) == 0) {  // tile-uniform
+        tile_aligned<SrcT, DstT, true>(s, d, n);
         return;
     }
     const SrcT* base = s - shift;
@@ -269,7 +289,7 @@ __device__ __forceinline__ void tile_general(const SrcT* s, DstT* d, int n, SrcT
 template <typename SrcT, typename DstT, bool kGeneral>
 __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable t) {
     constexpr int kTile = tile_elems<SrcT, DstT>();
-    __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral ? kTile + 16 : 8];
+    __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral && sizeof(SrcT) == 2 ? kTile + 16 : 8];
     const uint32_t tile = blockIdx.x;
     // wave-uniform lookup of the segment holding this tile
     uint32_t lo = 0, hi = t.nseg - 1;
@@ -352,12 +372,6 @@ __device__ __forceinline__ void add8(float* acc, u4 x, const ReduceArgs& a) {
 // one element.
 enum : int { kLdScalar = 0, kLdWord = 1, kLdHalf = 2 };
 
-typedef uint32_t u4w __attribute__((ext_vector_type(4), aligned(4)));
-
-__device__ __forceinline__ u4 ldw4(const uint16_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u4w*>(p));
-}
-
 // Rank r's elements j0 .. j0+7 (j0 a multiple of 8, all inside the rank's buffer),
 // read in two steps so that a batch of ranks issues all its loads before any shift.
 // kLdHalf: o = 1 when the buffer is only 2-byte aligned, else 0; the lane reads four
@@ -377,11 +391,11 @@ template <int kLd>
 __device__ __forceinline__ Raw load_raw(const ReduceArgs& a, int r, int64_t j0) {
     Raw x;
     if constexpr (kLd == kLdWord) {
-        x.v = ldw4(a.c[r] + j0);
+        x.v = ldu4w(a.c[r] + j0);
     } else {
         const int o = half_off(a.c[r]);
         const uint16_t* p = a.c[r] + j0 - o;  // dword aligned
-        x.v = ldw4(p);
+        x.v = ldu4w(p);
         x.w4 = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p + 6 + 2 * o));
     }
     return x;
