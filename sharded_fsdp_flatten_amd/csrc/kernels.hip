@@ -415,9 +415,13 @@ __device__ __forceinline__ u4 finish(const Raw& x, const ReduceArgs& a, int r) {
     }
 }
 
-template <int kLd>
-__device__ __forceinline__ u4 load_c(const ReduceArgs& a, int r, int64_t j0) {
-    return finish<kLd>(load_raw<kLd>(a, r, j0), a, r);
+__device__ __forceinline__ void load_out8(float* v, const float* out) {
+    const f4 lo = ld4(out), hi = ld4(out + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        v[q] = lo[q];
+        v[4 + q] = hi[q];
+    }
 }
 
 // Adds ranks [r, end) to acc in rank order, loading kAhead ranks before their adds.
@@ -432,7 +436,7 @@ __device__ __forceinline__ void add_ranks(float* acc, int r, int end, int64_t j0
 #pragma unroll
         for (int u = 0; u < kAhead; ++u) add8<kPre>(acc, finish<kLd>(x[u], a, r + u), a);
     }
-    for (; r < end; ++r) add8<kPre>(acc, load_c<kLd>(a, r, j0), a);
+    for (; r < end; ++r) add8<kPre>(acc, finish<kLd>(load_raw<kLd>(a, r, j0), a, r), a);
 }
 
 // One output, for buffers that are not 16-byte aligned and for the ragged last tile.
@@ -475,110 +479,110 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
     a.out[j] = acc;
 }
 
+// The 8 outputs j0 .. j0+7 of one lane over this launch's ranks.  kWhole: the tile
+// is whole, and its halves are swapped across lanes (ds_bpermute, no LDS
+// allocation) so that each store instruction writes 1 KiB of whole cache lines;
+// otherwise each lane stores its own 8.
+template <int kPre, int kLd, bool kHybrid, bool kAccum, bool kWhole>
+__device__ __forceinline__ void reduce_lane(const ReduceArgs& a, int64_t j0) {
+    constexpr int kEpt = 8;
+    constexpr int kAhead = FSDP_REDUCE_AHEAD;
+    float acc[kEpt];
+    if constexpr (!kHybrid) {
+        int r = 0;
+        if (a.first) {
+            set8<kPre>(acc, finish<kLd>(load_raw<kLd>(a, 0, j0), a, 0), a);
+            r = 1;
+        } else {
+            load_out8(acc, a.out + j0);
+        }
+        add_ranks<kPre, kLd>(acc, r, a.nc, j0, a);
+    } else {
+        // Loads run kAhead ranks ahead regardless of group boundaries; a wave-uniform
+        // position-in-group counter starts each group's sum at its first rank and
+        // folds it into the total after its last.
+        bool have = !a.first;
+        if (have) load_out8(acc, a.out + j0);
+        float s[kEpt];
+        int pos = 0;
+        for (int r = 0; r < a.nc; r += kAhead) {
+            const int n = min(kAhead, a.nc - r);
+            Raw x[kAhead];
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u)
+                if (u < n) x[u] = load_raw<kLd>(a, r + u, j0);
+#pragma unroll
+            for (int u = 0; u < kAhead; ++u) {
+                if (u >= n) break;
+                const u4 v = finish<kLd>(x[u], a, r + u);
+                if (pos == 0) set8<kPre>(s, v, a); else add8<kPre>(s, v, a);
+                if (++pos == a.group) {
+#pragma unroll
+                    for (int e = 0; e < kEpt; ++e) acc[e] = have ? acc[e] + s[e] : s[e];
+                    have = true;
+                    pos = 0;
+                }
+            }
+        }
+    }
+    if (a.last) {
+#pragma unroll
+        for (int e = 0; e < kEpt; ++e) acc[e] = acc[e] / a.post;
+        if constexpr (kAccum) {
+            float prev[kEpt];
+            load_out8(prev, a.out + j0);
+#pragma unroll
+            for (int e = 0; e < kEpt; ++e) acc[e] = prev[e] + acc[e];
+        }
+    }
+    if constexpr (kWhole) {
+        // lane l stores outputs 4l..4l+3 of each 256-output half of its wave's 512,
+        // which lane 32h + l/2 holds
+        const int lane = threadIdx.x & 63;
+        float* wave_out = a.out + (j0 - 8 * lane);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int src = 32 * h + (lane >> 1);
+            float w[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float lo = __shfl(acc[i], src, 64);
+                const float hi = __shfl(acc[4 + i], src, 64);
+                w[i] = (lane & 1) ? hi : lo;
+            }
+            st4(wave_out + 256 * h + 4 * lane, f4{w[0], w[1], w[2], w[3]});
+        }
+    } else {
+        st4(a.out + j0, f4{acc[0], acc[1], acc[2], acc[3]});
+        st4(a.out + j0 + 4, f4{acc[4], acc[5], acc[6], acc[7]});
+    }
+}
+
 // One tile of kReduceThreads * 8 outputs per workgroup.  Each lane owns 8
 // consecutive outputs; for every rank it loads their 8 bf16 as one 16-byte
 // vector (a wave reads 1 KiB contiguous per rank), kAhead ranks at a time, then
 // adds them strictly in rank order.  Hybrid: the same within each group of
 // ranks, then the group sums in group order.  kLd: how contributions are read
 // (the output is 16-byte aligned unless kLd is kLdScalar).
+// The tile that the output's end cuts runs first (workgroup 0), so that its longer
+// work overlaps the others': its lanes with 8 outputs take the vector path, then
+// the last len % 8 outputs take one lane each.
 template <int kPre, int kLd, bool kHybrid, bool kAccum>
 __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
     constexpr int kEpt = 8;
-    constexpr int kAhead = FSDP_REDUCE_AHEAD;
     constexpr int64_t kPerBlk = static_cast<int64_t>(kReduceThreads) * kEpt;
-    const int64_t blk = blockIdx.x;
+    const int64_t ntiles = (a.len + kPerBlk - 1) / kPerBlk;
+    int64_t blk = blockIdx.x;
+    if (a.len % kPerBlk != 0) blk = blk == 0 ? ntiles - 1 : blk - 1;
     if constexpr (kLd != kLdScalar) {
         const int64_t j0 = blk * kPerBlk + static_cast<int64_t>(threadIdx.x) * kEpt;
-        if (j0 + kEpt <= a.len) {
-            float acc[kEpt];
-            if constexpr (!kHybrid) {
-                int r = 0;
-                if (a.first) {
-                    set8<kPre>(acc, load_c<kLd>(a, 0, j0), a);
-                    r = 1;
-                } else {
-                    const f4 lo = ld4(a.out + j0), hi = ld4(a.out + j0 + 4);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[q] = lo[q];
-                        acc[4 + q] = hi[q];
-                    }
-                }
-                add_ranks<kPre, kLd>(acc, r, a.nc, j0, a);
-            } else {
-                // Loads run kAhead ranks ahead regardless of group boundaries; a
-                // wave-uniform position-in-group counter starts each group's sum at its
-                // first rank and folds it into the total after its last.
-                bool have = !a.first;
-                if (have) {
-                    const f4 lo = ld4(a.out + j0), hi = ld4(a.out + j0 + 4);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[q] = lo[q];
-                        acc[4 + q] = hi[q];
-                    }
-                }
-                float s[kEpt];
-                int pos = 0;
-                for (int r = 0; r < a.nc; r += kAhead) {
-                    const int cnt = min(kAhead, a.nc - r);
-                    Raw x[kAhead];
-#pragma unroll
-                    for (int u = 0; u < kAhead; ++u)
-                        if (u < cnt) x[u] = load_raw<kLd>(a, r + u, j0);
-#pragma unroll
-                    for (int u = 0; u < kAhead; ++u) {
-                        if (u >= cnt) break;
-                        const u4 v = finish<kLd>(x[u], a, r + u);
-                        if (pos == 0) set8<kPre>(s, v, a); else add8<kPre>(s, v, a);
-                        if (++pos == a.group) {
-#pragma unroll
-                            for (int e = 0; e < kEpt; ++e) acc[e] = have ? acc[e] + s[e] : s[e];
-                            have = true;
-                            pos = 0;
-                        }
-                    }
-                }
-            }
-            if (a.last) {
-#pragma unroll
-                for (int e = 0; e < kEpt; ++e) acc[e] = acc[e] / a.post;
-                if constexpr (kAccum) {
-                    const f4 lo = *reinterpret_cast<const f4*>(a.out + j0);
-                    const f4 hi = *reinterpret_cast<const f4*>(a.out + j0 + 4);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[q] = lo[q] + acc[q];
-                        acc[4 + q] = hi[q] + acc[4 + q];
-                    }
-                }
-            }
-            if (blk * kPerBlk + kPerBlk <= a.len) {
-                // Whole tile in the vector path: swap halves across lanes (ds_bpermute,
-                // no LDS allocation) so that each store instruction writes 1 KiB of
-                // whole cache lines; lane l stores outputs 4l..4l+3 of each 256-output
-                // half of its wave's 512, which lane 32h + l/2 holds.
-                const int lane = threadIdx.x & 63;
-                float* wave_out = a.out + blk * kPerBlk + (threadIdx.x & ~63) * kEpt;
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const int src = 32 * h + (lane >> 1);
-                    float w[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float lo = __shfl(acc[i], src, 64);
-                        const float hi = __shfl(acc[4 + i], src, 64);
-                        w[i] = (lane & 1) ? hi : lo;
-                    }
-                    st4(wave_out + 256 * h + 4 * lane, f4{w[0], w[1], w[2], w[3]});
-                }
-            } else {
-                st4(a.out + j0, f4{acc[0], acc[1], acc[2], acc[3]});
-                st4(a.out + j0 + 4, f4{acc[4], acc[5], acc[6], acc[7]});
-            }
-        } else {
-            for (int64_t j = j0; j < a.len && j < j0 + kEpt; ++j) reduce_one<kPre, kHybrid, kAccum>(a, j);
+        if (blk * kPerBlk + kPerBlk <= a.len) {
+            reduce_lane<kPre, kLd, kHybrid, kAccum, true>(a, j0);
+            return;
         }
+        if (j0 + kEpt <= a.len) reduce_lane<kPre, kLd, kHybrid, kAccum, false>(a, j0);
+        const int64_t j = (a.len & ~static_cast<int64_t>(kEpt - 1)) + threadIdx.x;
+        if (j < a.len) reduce_one<kPre, kHybrid, kAccum>(a, j);
     } else {
 #pragma unroll
         for (int e = 0; e < kEpt; ++e) {
