@@ -82,6 +82,12 @@ def _load():
         lib.orc_grad_reduce_ex.restype = None
         lib.orc_grad_accumulate.argtypes = [_i64, _p, _p, ctypes.c_int]
         lib.orc_grad_accumulate.restype = None
+        lib.orc_grad_unscale.argtypes = [_i64, _p, ctypes.c_float, _p]
+        lib.orc_grad_unscale.restype = None
+        lib.orc_flat_sqnorm.argtypes = [_i32, _p, _i64, _i64, _p, _p]
+        lib.orc_flat_sqnorm.restype = None
+        lib.orc_rows_sqnorm.argtypes = [_i32, _p, _p, _i64, _i64, _p, _p]
+        lib.orc_rows_sqnorm.restype = None
         _lib = lib
     return _lib
 
@@ -330,3 +336,39 @@ def grad_accumulate(grad_bf16: np.ndarray, acc: np.ndarray, init: bool) -> np.nd
         raise ValueError("acc must be a contiguous float32 array of the gradient's length")
     _load().orc_grad_accumulate(g.size, _ptr(g), _ptr(acc), 1 if init else 0)
     return acc
+
+
+def grad_unscale(grad: np.ndarray, inv_scale: float, found_inf: np.ndarray) -> np.ndarray:
+    """grad *= inv_scale in place (binary32); found_inf[0] = 1 if any input is not finite
+    (never cleared here)."""
+    if grad.dtype != np.float32 or not grad.flags["C_CONTIGUOUS"]:
+        raise ValueError("grad must be a contiguous float32 array")
+    if found_inf.dtype != np.float32 or found_inf.size != 1:
+        raise ValueError("found_inf must be one float32")
+    _load().orc_grad_unscale(grad.size, _ptr(grad), ctypes.c_float(inv_scale), _ptr(found_inf))
+    return grad
+
+
+def flat_sqnorm(shapes: Sequence[Sequence[int]], N: int, k: int, shard: np.ndarray) -> np.ndarray:
+    """Per-parameter sums of squares (float64) of rank k's FLAT gradient shard."""
+    g = _f32(shard).reshape(-1)
+    n = _i64_array(numel(s) for s in shapes)
+    T, S, L, pad = flat_sizes(n, N)
+    if g.size != S or not 0 <= k < N:
+        raise ValueError("shard must hold S elements of a rank in [0, N)")
+    out = np.zeros(len(shapes), dtype=np.float64)
+    _load().orc_flat_sqnorm(len(shapes), _ptr(n), N, k, _ptr(g), _ptr(out))
+    return out
+
+
+def rows_sqnorm(shapes: Sequence[Sequence[int]], N: int, k: int, seg: np.ndarray) -> np.ndarray:
+    """Per-parameter sums of squares (float64) of rank k's FSDP2 gradient segment."""
+    g = _f32(seg).reshape(-1)
+    mr = [rows_of(s) for s in shapes]
+    m = _i64_array(a for a, _ in mr)
+    r = _i64_array(b for _, b in mr)
+    if g.size != rows_sizes(shapes, N) or not 0 <= k < N:
+        raise ValueError("seg must hold P_r elements of a rank in [0, N)")
+    out = np.zeros(len(shapes), dtype=np.float64)
+    _load().orc_rows_sqnorm(len(shapes), _ptr(m), _ptr(r), N, k, _ptr(g), _ptr(out))
+    return out

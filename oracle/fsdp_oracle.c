@@ -434,3 +434,78 @@ void orc_grad_accumulate(int64_t n, const uint16_t* grad, float* acc, int init) 
         acc[j] = init ? g : acc[j] + g;
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* Sharded optimizer statistics (per-rank halves)                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Sharded gradient scaler, the per-rank half ([P1] section 3.4 "Native Mixed
+ * Precision and the Sharded Gradient Scaler"): every rank unscales its own
+ * gradient shard by the one global factor and records whether the shard holds
+ * an overflow; the ranks then combine their flags (a max all-reduce) so that
+ * all of them take or skip the step together.  Readings taken (the pages give
+ * no implementation): the gradient is multiplied by inv_scale = 1/scale (one
+ * rounded binary32 multiply per element); the check looks at the value before
+ * it is multiplied; the flag is a float that is set to 1 when a non-finite
+ * value is seen and is never cleared here (the caller clears it, so several
+ * shards can share one flag).
+ */
+void orc_grad_unscale(int64_t n, float* g, float inv_scale, float* found_inf) {
+    for (int64_t j = 0; j < n; ++j) {
+        float x = g[j];
+        if (!isfinite(x)) *found_inf = 1.0f;
+        g[j] = x * inv_scale;
+    }
+}
+
+/*
+ * Per-parameter sums of squares of rank k's FLAT gradient shard.  The pages
+ * warn that statistics of original parameters (norms for gradient clipping,
+ * per-parameter optimizer statistics) "become invalid" when computed on flat
+ * shards, because a shard ignores parameter boundaries ([P1] section 6
+ * "Limitations", the mathematical-equivalence caveat).  The unit's layout
+ * knows the boundaries: every shard element [kS, (k+1)S) of the flat buffer is
+ * attributed to the parameter it came from (padding to none), and
+ *   out[i] = sum of g_j^2 over the shard elements of parameter i,
+ * with each square and each addition in binary64 (the square of a binary32 is
+ * exact in binary64), in shard order.  Summed over the N ranks (an all-reduce
+ * of p numbers) out[i] is parameter i's squared gradient norm; the sum over i
+ * is the global one.
+ */
+void orc_flat_sqnorm(int32_t p, const int64_t* numel, int64_t N, int64_t k, const float* shard,
+                     double* out) {
+    int64_t T = 0;
+    for (int32_t i = 0; i < p; ++i) T += numel[i];
+    int64_t S = ceil_div(T, N);
+    for (int32_t i = 0; i < p; ++i) out[i] = 0.0;
+    int32_t i = 0;
+    int64_t off = 0; /* start of parameter i in the flat buffer */
+    for (int64_t j = 0; j < S; ++j) {
+        int64_t g = k * S + j;
+        if (g >= T) break; /* padding */
+        while (g >= off + numel[i]) { off += numel[i]; ++i; }
+        double x = (double)shard[j];
+        out[i] = out[i] + x * x;
+    }
+}
+
+/*
+ * The same for rank k's FSDP2 segment: parameter i occupies, from offset q_i,
+ * the rows of the rank's chunk followed by zero rows up to c_i; only the rows
+ * the rank holds count.
+ */
+void orc_rows_sqnorm(int32_t p, const int64_t* m, const int64_t* r, int64_t N, int64_t k,
+                     const float* seg, double* out) {
+    int64_t q = 0;
+    for (int32_t i = 0; i < p; ++i) {
+        int64_t c = ceil_div(m[i], N);
+        int64_t rows = min64(m[i], (k + 1) * c) - min64(m[i], k * c);
+        out[i] = 0.0;
+        for (int64_t e = 0; e < rows * r[i]; ++e) {
+            double x = (double)seg[q + e];
+            out[i] = out[i] + x * x;
+        }
+        q += c * r[i];
+    }
+}
