@@ -174,25 +174,36 @@ def cpu_baseline(host, unit, N, k, S, valid, pre, post, hp, rows):
 
 def time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows, grad, outs,
                    gathered, adam_p, stream, flush=None):
-    """The next rows, in an order where no kernel reads what the previous one just wrote:
+    """The next rows, in an order where no kernel reads what one of the last few wrote:
     hybrid reduction (groups of 8 ranks) accumulating into the grad shard; copy-in of
-    per-parameter bf16 gradients into the ReduceScatter input (all ranks); cast of rank k's
-    fp32 shard to bf16; bf16 copy-out of a gathered bf16 unit; local fp32 accumulation of an
-    unsharded bf16 gradient.  Reuses the step's buffers as inputs (values do not matter)."""
+    per-parameter bf16 gradients into the ReduceScatter input (all ranks); unscale of the
+    grad shard (sharded gradient scaler); cast of rank k's fp32 shard to bf16; bf16
+    copy-out of a gathered bf16 unit; local fp32 accumulation of an unsharded bf16
+    gradient; per-parameter sums of squares of the grad shard.  Reuses the step's buffers
+    as inputs (values do not matter)."""
     import torch
     dev = grad.device
     rs_input = torch.empty(L, dtype=torch.bfloat16, device=dev)
     shard16 = torch.empty(S, dtype=torch.bfloat16, device=dev)
     group = 8 if N % 8 == 0 and N > 8 else 0
+    flag = torch.zeros(1, device=dev)
+    sq_ws = torch.empty(max(1, B.fsdp_grad_sqnorm_workspace(u, k)), dtype=torch.float64, device=dev)
+    sq_out = torch.empty(len(unit.shapes), dtype=torch.float64, device=dev)
+    valid = u.info(k)["valid"]
     rows = {
         "grad_reduce_hybrid_accumulate": (lambda: B.fsdp_grad_reduce_shard_ex(
             u, contrib_rows, pre, post, grad, group=group, accumulate=True), (2 * N + 8) * S, S),
         "copyin_bf16_all_ranks": (lambda: B.fsdp_flatten_shard_bf16(
             u, outs, B.FSDP_ALL_RANKS, rs_input), 2 * T + 2 * L, L),
+        # inv_scale 1 keeps the shard's values from one repetition to the next
+        "grad_unscale_rank": (lambda: B.fsdp_grad_unscale(u, k, grad, 1.0, flag), 8 * S, S),
         "cast_to_bf16_rank": (lambda: B.fsdp_cast_to_bf16(u, k, adam_p, shard16), 6 * S, S),
         "copyout_bf16": (lambda: B.fsdp_unflatten_copyout_bf16(u, rs_input, outs), 4 * T, T),
         "grad_accumulate_all": (lambda: B.fsdp_grad_accumulate(
             u, B.FSDP_ALL_RANKS, rs_input, gathered, False), 10 * L, L),
+        # algorithmic bytes: the shard's real elements (8 bytes per 4096-element tile of
+        # partial sums, written and read back, are not counted)
+        "grad_sqnorm_rank": (lambda: B.fsdp_grad_sqnorm(u, k, grad, sq_out, sq_ws), 4 * valid, valid),
     }
     order = list(rows)
     for _ in range(max(1, args.warmup)):
@@ -221,7 +232,7 @@ def time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows, gra
                   "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                   "elements_per_s": float("%.4g" % (elems / (ms * 1e-3))), "reps": reps}
     out["hybrid_group"] = group
-    del rs_input, shard16
+    del rs_input, shard16, sq_ws, sq_out, flag
     return out
 
 

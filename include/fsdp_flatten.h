@@ -52,7 +52,7 @@ extern "C" {
 #define FSDP_API
 #endif
 
-#define FSDP_ABI_VERSION 1
+#define FSDP_ABI_VERSION 2
 #define FSDP_ALL_RANKS (-1)
 #define FSDP_MAX_NDIM 8
 
@@ -308,6 +308,59 @@ FSDP_API fsdp_status fsdp_grad_reduce_shard_ex(const fsdp_unit* unit, const uint
  */
 FSDP_API fsdp_status fsdp_grad_accumulate(const fsdp_unit* unit, int32_t k, const uint16_t* grad,
                                           float* acc, int32_t init, void* stream);
+
+/*
+ * Sharded gradient scaler, the per-rank half ([P1] section 3.4 "Native Mixed
+ * Precision and the Sharded Gradient Scaler": the scale is global, so every
+ * rank unscales its own shard by the same factor, and overflow detection must
+ * be combined across ranks so that all of them skip or take the step):
+ *   grad[j] = grad[j] * inv_scale   (one rounded binary32 multiply)
+ * over rank k's shard (S elements) or, with k == FSDP_ALL_RANKS, the whole
+ * layout (L elements), and *found_inf = 1.0f if any grad[j] was not finite
+ * before the multiply.  The flag is never cleared here: the caller zeroes it,
+ * may share it between several shards, and combines it across ranks (a max
+ * all-reduce).
+ *   grad      : device pointer, fp32, updated in place.
+ *   inv_scale : finite.
+ *   found_inf : device pointer to one float.
+ * Errors: FSDP_E_ARG (NULL unit, grad or found_inf; inv_scale not finite),
+ * FSDP_E_RANGE (k), FSDP_E_ALIGN, FSDP_E_HIP.  With no elements (an empty
+ * unit) nothing is launched and grad and found_inf may be NULL.
+ */
+FSDP_API fsdp_status fsdp_grad_unscale(const fsdp_unit* unit, int32_t k, float* grad,
+                                       float inv_scale, float* found_inf, void* stream);
+
+/* Doubles of workspace fsdp_grad_sqnorm needs for rank k (k in [0, N)):
+ * one binary64 partial per 4096-element tile of each parameter's run. */
+FSDP_API fsdp_status fsdp_grad_sqnorm_workspace(const fsdp_unit* unit, int32_t k,
+                                                int64_t* n_doubles);
+
+/*
+ * Per-parameter sums of squares of rank k's gradient shard.  The pages note
+ * that statistics of original parameters (gradient-clipping norms, per-
+ * parameter optimizer statistics) "become invalid" on flat shards, which
+ * ignore parameter boundaries ([P1] section 6, the mathematical-equivalence
+ * limitation).  The unit plan knows the boundaries, so
+ *   out[i] = sum of grad[j]^2 over the shard elements of parameter i
+ * (padding belongs to no parameter; FSDP2 zero rows are not counted), each
+ * square and sum in binary64.  Summed over the N ranks (one all-reduce of
+ * n_params doubles) out[i] is parameter i's squared gradient norm, and the
+ * sum over i the global squared norm that clipping needs.
+ * Deterministic for a given unit and rank: every tile is summed in a fixed
+ * order into the workspace, then each parameter's tiles in a fixed order.
+ *   grad      : device pointer, fp32, S elements (k in [0, N)).
+ *   workspace : device pointer, at least fsdp_grad_sqnorm_workspace doubles,
+ *               overwritten; workspace_len its length in doubles.
+ *   out       : device pointer, n_params doubles, written (0 for parameters
+ *               the rank holds none of).
+ * Calls that share a workspace on one stream run in order; on different
+ * streams they must not share one.
+ * Errors: FSDP_E_ARG (NULL pointers), FSDP_E_RANGE (k, or workspace_len too
+ * small), FSDP_E_ALIGN, FSDP_E_HIP.
+ */
+FSDP_API fsdp_status fsdp_grad_sqnorm(const fsdp_unit* unit, int32_t k, const float* grad,
+                                      double* workspace, int64_t workspace_len, double* out,
+                                      void* stream);
 
 #ifdef __cplusplus
 }

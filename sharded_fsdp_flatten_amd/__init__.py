@@ -18,6 +18,9 @@ from .binding import (  # noqa: F401
     fsdp_grad_accumulate,
     fsdp_grad_reduce_shard,
     fsdp_grad_reduce_shard_ex,
+    fsdp_grad_sqnorm,
+    fsdp_grad_sqnorm_workspace,
+    fsdp_grad_unscale,
     fsdp_last_error,
     fsdp_status_string,
     fsdp_unflatten_copyout,

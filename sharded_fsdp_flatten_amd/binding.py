@@ -104,6 +104,12 @@ def load() -> ctypes.CDLL:
     lib.fsdp_grad_reduce_shard_ex.restype = st
     lib.fsdp_grad_accumulate.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp]
     lib.fsdp_grad_accumulate.restype = st
+    lib.fsdp_grad_unscale.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp]
+    lib.fsdp_grad_unscale.restype = st
+    lib.fsdp_grad_sqnorm_workspace.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
+    lib.fsdp_grad_sqnorm_workspace.restype = st
+    lib.fsdp_grad_sqnorm.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int64, _vp, _vp]
+    lib.fsdp_grad_sqnorm.restype = st
     _lib = lib
     return lib
 
@@ -371,8 +377,41 @@ def fsdp_grad_accumulate(unit: Unit, k: int, grad, acc, init: bool, stream=None)
                                        _stream(stream, grad, acc)))
 
 
+_F64 = ("torch.float64",)
+
+
+def fsdp_grad_unscale(unit: Unit, k: int, grad, inv_scale: float, found_inf, stream=None) -> None:
+    """grad *= inv_scale over rank k's shard or (FSDP_ALL_RANKS) all L; found_inf (one
+    float) is set to 1 if any input was not finite, never cleared."""
+    n = unit.L if k == FSDP_ALL_RANKS else unit.S
+    _need(grad, n, "grad")
+    _need(found_inf, 1, "found_inf")
+    _check(load().fsdp_grad_unscale(unit.handle, k, _addr(grad, _F32) or None, inv_scale,
+                                    _addr(found_inf, _F32) or None, _stream(stream, grad)))
+
+
+def fsdp_grad_sqnorm_workspace(unit: Unit, k: int) -> int:
+    """Doubles of workspace fsdp_grad_sqnorm needs for rank k."""
+    n = ctypes.c_int64()
+    _check(load().fsdp_grad_sqnorm_workspace(unit.handle, k, ctypes.byref(n)))
+    return int(n.value)
+
+
+def fsdp_grad_sqnorm(unit: Unit, k: int, grad, out, workspace, stream=None) -> None:
+    """out[i] = sum of squares (float64) of parameter i's elements in rank k's shard."""
+    need = fsdp_grad_sqnorm_workspace(unit, k)
+    _need(grad, unit.S, "grad")
+    _need(out, len(unit.shapes), "out")
+    _need(workspace, need, "workspace")
+    ws_len = workspace.numel() if _is_tensor(workspace) else need
+    _check(load().fsdp_grad_sqnorm(unit.handle, k, _addr(grad, _F32) or None,
+                                   _addr(workspace, _F64) or None, ws_len,
+                                   _addr(out, _F64) or None, _stream(stream, grad)))
+
+
 ABI_FUNCTIONS = ["fsdp_abi_version", "fsdp_last_error", "fsdp_status_string", "fsdp_unit_create",
                  "fsdp_unit_destroy", "fsdp_unit_info", "fsdp_unit_param_offset", "fsdp_unit_recv_pitch",
                  "fsdp_flatten_shard", "fsdp_unflatten_copyout", "fsdp_grad_reduce_shard",
                  "fsdp_adam_shard", "fsdp_cast_to_bf16", "fsdp_unflatten_copyout_bf16",
-                 "fsdp_flatten_shard_bf16", "fsdp_grad_reduce_shard_ex", "fsdp_grad_accumulate"]
+                 "fsdp_flatten_shard_bf16", "fsdp_grad_reduce_shard_ex", "fsdp_grad_accumulate",
+                 "fsdp_grad_unscale", "fsdp_grad_sqnorm_workspace", "fsdp_grad_sqnorm"]

@@ -372,4 +372,54 @@ fsdp_status fsdp_grad_accumulate(const fsdp_unit* unit, int32_t k, const uint16_
     return ok();
 }
 
+fsdp_status fsdp_grad_unscale(const fsdp_unit* unit, int32_t k, float* grad, float inv_scale,
+                              float* found_inf, void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    fsdp_status s;
+    if ((s = check_rank(u, k)) != FSDP_OK) return s;
+    if (!std::isfinite(inv_scale)) return fail(FSDP_E_ARG, "inv_scale must be finite");
+    const int64_t n = k == FSDP_ALL_RANKS ? u.L : u.S;
+    if ((s = check_buf(grad, n, sizeof(float), "grad")) != FSDP_OK) return s;
+    if (n == 0) return ok();
+    if ((s = check_buf(found_inf, 1, sizeof(float), "found_inf")) != FSDP_OK) return s;
+    const hipError_t e = fsdp::launch_grad_unscale(grad, n, inv_scale, found_inf,
+                                                   static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_grad_unscale launch");
+    return ok();
+}
+
+fsdp_status fsdp_grad_sqnorm_workspace(const fsdp_unit* unit, int32_t k, int64_t* n_doubles) {
+    if (!unit || !n_doubles) return fail(FSDP_E_ARG, "unit and n_doubles must not be NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    if (k < 0 || k >= u.N) return fail(FSDP_E_RANGE, "k must be in [0, N)");
+    std::vector<fsdp::ParamRun> runs;
+    fsdp::plan_param_runs(u, k, &runs);
+    *n_doubles = fsdp::sqnorm_tiles(runs);
+    return ok();
+}
+
+fsdp_status fsdp_grad_sqnorm(const fsdp_unit* unit, int32_t k, const float* grad,
+                             double* workspace, int64_t workspace_len, double* out, void* stream) {
+    if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+    const fsdp::UnitPlan& u = unit->plan;
+    if (k < 0 || k >= u.N) return fail(FSDP_E_RANGE, "k must be in [0, N)");
+    std::vector<fsdp::ParamRun> runs;
+    fsdp::plan_param_runs(u, k, &runs);
+    const int64_t need = fsdp::sqnorm_tiles(runs);
+    fsdp_status s;
+    if ((s = check_buf(grad, u.S, sizeof(float), "grad")) != FSDP_OK) return s;
+    if ((s = check_buf(out, static_cast<int64_t>(runs.size()), sizeof(double), "out")) != FSDP_OK)
+        return s;
+    if (workspace_len < need)
+        return fail(FSDP_E_RANGE, "workspace holds " + std::to_string(workspace_len) +
+                                      " doubles; this rank needs " + std::to_string(need));
+    if ((s = check_buf(workspace, need, sizeof(double), "workspace")) != FSDP_OK) return s;
+    if (runs.empty()) return ok();
+    const hipError_t e = fsdp::launch_grad_sqnorm(grad, runs, workspace, out,
+                                                  static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "fsdp_grad_sqnorm launch");
+    return ok();
+}
+
 }  // extern "C"

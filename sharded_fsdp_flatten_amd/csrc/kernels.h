@@ -37,4 +37,17 @@ struct AdamScalars {
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* pb, int64_t len,
                         const AdamScalars& s, hipStream_t stream);
 
+// g *= inv_scale over len elements, in place; *found_inf = 1 if any input is not
+// finite (never cleared).
+hipError_t launch_grad_unscale(float* g, int64_t len, float inv_scale, float* found_inf,
+                               hipStream_t stream);
+
+// Tiles (= binary64 partial sums held in the workspace) of a sum of squares over runs.
+int64_t sqnorm_tiles(const std::vector<ParamRun>& runs);
+
+// out[i] = sum of g[runs[i].offset + j]^2 over j < runs[i].n, in binary64, for every
+// run i (0 for an empty run); `partial` holds sqnorm_tiles(runs) doubles.
+hipError_t launch_grad_sqnorm(const float* g, const std::vector<ParamRun>& runs, double* partial,
+                              double* out, hipStream_t stream);
+
 }  // namespace fsdp

@@ -70,6 +70,9 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #ifndef FSDP_ACC_VPL
 #define FSDP_ACC_VPL 4          // 4-element vectors per lane in the local accumulation (1/2/4: 5.70/5.96/6.07 TB/s)
 #endif
+#ifndef FSDP_UNSCALE_VPL
+#define FSDP_UNSCALE_VPL 4      // 4-element vectors per lane in the gradient unscale
+#endif
 #ifndef FSDP_ACC_NT
 #define FSDP_ACC_NT 1       // local accumulation: nt measured faster (5.9 vs 5.6 TB/s)
 #endif
@@ -788,6 +791,133 @@ void launch_reduce_mode(const ReduceArgs& a, bool hybrid, bool accum, dim3 grid,
     }
 }
 
+// ---------------------------------------------------------------------------
+// sharded gradient scaler: g *= inv_scale, flag non-finite inputs
+// ---------------------------------------------------------------------------
+// In place: plain loads and nt stores (as AdamW).  A wave that saw a non-finite
+// input has one lane store 1.0f into the flag (vector store; every writer stores
+// the same value, so concurrent stores agree).
+template <bool kVec>
+__global__ __launch_bounds__(kThreads) void unscale_kernel(float* __restrict__ g, int64_t len,
+                                                           float inv, float* __restrict__ found) {
+    constexpr int kV = FSDP_UNSCALE_VPL;
+    constexpr int64_t kPerBlk = static_cast<int64_t>(kThreads) * 4 * kV;
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kPerBlk;
+    bool bad = false;
+    if (kVec && base + kPerBlk <= len) {
+        f4 x[kV];
+#pragma unroll
+        for (int h = 0; h < kV; ++h) x[h] = *reinterpret_cast<const f4*>(g + base + 4 * (threadIdx.x + h * kThreads));
+#pragma unroll
+        for (int h = 0; h < kV; ++h) {
+            f4 y;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bad = bad || !__builtin_isfinite(x[h][q]);
+                y[q] = x[h][q] * inv;
+            }
+            st4(g + base + 4 * (threadIdx.x + h * kThreads), y);
+        }
+    } else {
+        for (int e = 0; e < 4 * kV; ++e) {
+            const int64_t j = base + static_cast<int64_t>(e) * kThreads + threadIdx.x;
+            if (j < len) {
+                const float x = g[j];
+                bad = bad || !__builtin_isfinite(x);
+                g[j] = x * inv;
+            }
+        }
+    }
+    const uint64_t mask = __ballot(bad);
+    if (mask != 0 && (threadIdx.x & 63) == static_cast<unsigned>(__builtin_ctzll(mask))) *found = 1.0f;
+}
+
+// ---------------------------------------------------------------------------
+// per-parameter sums of squares of a gradient shard, in binary64
+// ---------------------------------------------------------------------------
+constexpr int kSqThreads = 256;
+constexpr int kSqPerThread = 16;  // four 4-float vectors
+constexpr int64_t kSqTile = static_cast<int64_t>(kSqThreads) * kSqPerThread;
+
+struct SqRun {
+    int64_t offset;   // first element of the run in the shard
+    int64_t n;        // elements
+    uint32_t tile0;   // first workspace slot
+    uint32_t ntiles;
+    int32_t out;      // parameter index
+    int32_t unused;
+};
+struct SqTable {
+    const float* g;
+    double* partial;
+    double* out;
+    uint32_t nrun;
+    uint32_t unused;
+    SqRun run[kMaxSegs];
+};
+static_assert(sizeof(SqTable) <= 4096, "run table must fit one kernel argument block");
+
+// Block sum of one double per thread, in a fixed order: a shuffle tree inside each
+// wave, then the waves' sums in wave order.  Returns the sum in thread 0.
+__device__ __forceinline__ double block_sum(double v, double* lds) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = v + __shfl_down(v, o, 64);
+    if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0)
+        for (int w = 0; w < kSqThreads / 64; ++w) s = s + lds[w];
+    return s;
+}
+
+// Stage 1: one tile of one run per workgroup -> one partial sum.  Each lane adds
+// the squares of its 16 elements in order (a binary32 square is exact in binary64).
+// Loads need dword alignment only (runs start at any element).
+__global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(SqTable t) {
+    __shared__ double lds[kSqThreads / 64];
+    const uint32_t tile = blockIdx.x;
+    uint32_t lo = 0, hi = t.nrun - 1;  // wave-uniform: last non-empty run with tile0 <= tile
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (t.run[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
+    }
+    const SqRun& r = t.run[lo];
+    const int64_t e0 = static_cast<int64_t>(tile - r.tile0) * kSqTile;
+    const int64_t n = min(kSqTile, r.n - e0);
+    const float* g = t.g + r.offset + e0;
+    double acc = 0.0;
+    if (n == kSqTile) {
+        f4 x[kSqPerThread / 4];
+#pragma unroll
+        for (int h = 0; h < kSqPerThread / 4; ++h) x[h] = ld4w(g + 4 * (threadIdx.x + h * kSqThreads));
+#pragma unroll
+        for (int h = 0; h < kSqPerThread / 4; ++h)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const double d = static_cast<double>(x[h][q]);
+                acc = acc + d * d;
+            }
+    } else {
+        for (int64_t e = threadIdx.x; e < n; e += kSqThreads) {
+            const double d = static_cast<double>(g[e]);
+            acc = acc + d * d;
+        }
+    }
+    const double s = block_sum(acc, lds);
+    if (threadIdx.x == 0) t.partial[tile] = s;
+}
+
+// Stage 2: one workgroup per run sums its partials in a fixed order (lane order
+// within strided passes, then the block tree) and writes the parameter's result.
+__global__ __launch_bounds__(kSqThreads) void sqnorm_final_kernel(SqTable t) {
+    __shared__ double lds[kSqThreads / 64];
+    const SqRun& r = t.run[blockIdx.x];
+    double acc = 0.0;
+    for (uint32_t i = threadIdx.x; i < r.ntiles; i += kSqThreads) acc = acc + t.partial[r.tile0 + i];
+    const double s = block_sum(acc, lds);
+    if (threadIdx.x == 0) t.out[r.out] = s;
+}
+
 }  // namespace
 
 hipError_t launch_segcopy(const std::vector<CopySeg>& segs, Pipe pipe, hipStream_t stream) {
@@ -901,4 +1031,63 @@ hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* 
     return hipGetLastError();
 }
 
+hipError_t launch_grad_unscale(float* g, int64_t len, float inv_scale, float* found_inf,
+                               hipStream_t stream) {
+    if (len <= 0) return hipSuccess;
+    const int64_t per_blk = static_cast<int64_t>(kThreads) * 4 * FSDP_UNSCALE_VPL;
+    const int64_t blocks = (len + per_blk - 1) / per_blk;
+    if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
+    const dim3 grid = grid_of(blocks), block(kThreads);
+    if (aligned_to(g, 16))
+        hipLaunchKernelGGL((unscale_kernel<true>), grid, block, 0, stream, g, len, inv_scale, found_inf);
+    else
+        hipLaunchKernelGGL((unscale_kernel<false>), grid, block, 0, stream, g, len, inv_scale, found_inf);
+    return hipGetLastError();
+}
+
+int64_t sqnorm_tiles(const std::vector<ParamRun>& runs) {
+    int64_t n = 0;
+    for (const ParamRun& r : runs) n += (r.n + kSqTile - 1) / kSqTile;
+    return n;
+}
+
+hipError_t launch_grad_sqnorm(const float* g, const std::vector<ParamRun>& runs, double* partial,
+                              double* out, hipStream_t stream) {
+    // Runs go kMaxSegs to a launch pair; workspace slots are numbered across all runs.
+    int64_t slot = 0;
+    for (size_t i0 = 0; i0 < runs.size(); i0 += kMaxSegs) {
+        const size_t i1 = std::min(runs.size(), i0 + static_cast<size_t>(kMaxSegs));
+        SqTable all{}, busy{};  // every run of the batch / only the non-empty ones
+        all.g = busy.g = g;
+        all.partial = busy.partial = partial;
+        all.out = busy.out = out;
+        uint32_t tiles = 0;
+        for (size_t i = i0; i < i1; ++i) {
+            const int64_t nt = (runs[i].n + kSqTile - 1) / kSqTile;
+            if (slot + nt > 0xFFFFFFFFll) return hipErrorInvalidValue;
+            SqRun r{runs[i].offset, runs[i].n, static_cast<uint32_t>(slot),
+                    static_cast<uint32_t>(nt), static_cast<int32_t>(i), 0};
+            all.run[all.nrun++] = r;
+            if (nt > 0) busy.run[busy.nrun++] = r;
+            slot += nt;
+            tiles += static_cast<uint32_t>(nt);
+        }
+        // tiles of this batch are workspace slots [first, first + tiles): stage 1 uses
+        // the tile index relative to the batch's first slot
+        if (busy.nrun > 0) {
+            const uint32_t first = busy.run[0].tile0;
+            for (uint32_t j = 0; j < busy.nrun; ++j) busy.run[j].tile0 -= first;
+            busy.partial = partial + first;
+            hipLaunchKernelGGL(sqnorm_partial_kernel, grid_of(tiles), dim3(kSqThreads), 0, stream, busy);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+        hipLaunchKernelGGL(sqnorm_final_kernel, dim3(all.nrun), dim3(kSqThreads), 0, stream, all);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
 }  // namespace fsdp
+

@@ -301,4 +301,25 @@ void plan_whole(const UnitPlan& u, int64_t k, const void* src, void* dst,
     segs->push_back(s);
 }
 
+void plan_param_runs(const UnitPlan& u, int64_t k, std::vector<ParamRun>* runs) {
+    runs->assign(u.params.size(), ParamRun{});
+    for (size_t i = 0; i < u.params.size(); ++i) {
+        const ParamPlan& p = u.params[i];
+        ParamRun& run = (*runs)[i];
+        if (u.layout == kFlat) {
+            const int64_t lo = std::max(p.offset, k * u.S);
+            const int64_t hi = std::min(p.offset + p.numel, (k + 1) * u.S);
+            if (hi > lo) {
+                run.offset = lo - k * u.S;
+                run.n = hi - lo;
+            }
+        } else {
+            int64_t lo, hi;
+            rank_rows(p, k, &lo, &hi);
+            run.offset = p.offset;
+            run.n = (hi - lo) * p.row_len;
+        }
+    }
+}
+
 }  // namespace fsdp

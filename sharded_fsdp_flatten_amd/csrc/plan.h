@@ -69,5 +69,14 @@ void plan_copyout(const UnitPlan& u, const void* gathered, size_t src_esize, voi
 // src and dst index the same positions.
 void plan_whole(const UnitPlan& u, int64_t k, const void* src, void* dst,
                 std::vector<CopySeg>* segs);
+// Where each parameter's real elements sit inside rank k's shard (k in [0, N)):
+// run i starts `offset` elements into the shard and holds `n` of parameter i's
+// elements (n = 0 when the rank holds none).  FLAT: the intersection of the
+// parameter's range with [kS, (k+1)S); ROWS: the rows of the rank's chunk, from q_i.
+struct ParamRun {
+    int64_t offset = 0;
+    int64_t n = 0;
+};
+void plan_param_runs(const UnitPlan& u, int64_t k, std::vector<ParamRun>* runs);
 
 }  // namespace fsdp

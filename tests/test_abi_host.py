@@ -378,3 +378,64 @@ def test_next_rows_noops_on_empty_units(B):
             B.fsdp_grad_reduce_shard_ex(u, [0] * 4, 1.0, 1.0, 0, group=2, accumulate=True, stream=0)
             B.fsdp_grad_accumulate(u, B.FSDP_ALL_RANKS, 0, 0, True, stream=0)
             assert B.fsdp_last_error() == ""
+
+
+def _runs_by_hand(shapes, N, k, layout_flat=True):
+    """Each parameter's element count inside rank k's shard, from the layout definitions."""
+    import oracle
+    if layout_flat:
+        numels = [oracle.numel(sh) for sh in shapes]
+        T, S, L, pad = oracle.flat_sizes(numels, N)
+        out, off = [], 0
+        for n in numels:
+            lo, hi = max(off, k * S), min(off + n, (k + 1) * S)
+            out.append(max(0, hi - lo))
+            off += n
+        return out
+    out = []
+    for sh in shapes:
+        m, r = oracle.rows_of(sh)
+        c = -(-m // N)
+        out.append((min(m, (k + 1) * c) - min(m, k * c)) * r)
+    return out
+
+
+def test_sqnorm_workspace_counts_4096_element_tiles_per_parameter(B):
+    for layout, shapes, N in [(B.FSDP_FLAT, W.gpt2_large_block().shapes, 8),
+                              (B.FSDP_FLAT, W.gpt175b_block().shapes, 128),
+                              (B.FSDP_ROWS, W.gpt2_large_emb_rows().shapes, 8),
+                              (B.FSDP_FLAT, [(3, 4), (3,)], 16), (B.FSDP_FLAT, [(5000,), (3,)], 2)]:
+        u = B.fsdp_unit_create(layout, shapes, N)
+        for k in sorted({0, 1, N // 2, N - 1}):
+            runs = _runs_by_hand(shapes, N, k, layout == B.FSDP_FLAT)
+            assert B.fsdp_grad_sqnorm_workspace(u, k) == sum(-(-n // 4096) for n in runs)
+
+
+def test_unscale_and_sqnorm_errors(B):
+    import ctypes
+    lib = B.load()
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(4,), (3,)], 2)
+    g, f, o, w = 0x1000, 0x2000, 0x3000, 0x4000  # never dereferenced: validation fails first
+    assert lib.fsdp_grad_unscale(None, 0, g, 0.5, f, None) == 1
+    assert lib.fsdp_grad_unscale(u.handle, 2, g, 0.5, f, None) == 2
+    assert lib.fsdp_grad_unscale(u.handle, 0, None, 0.5, f, None) == 1
+    assert lib.fsdp_grad_unscale(u.handle, 0, g, 0.5, None, None) == 1
+    assert lib.fsdp_grad_unscale(u.handle, 0, g + 2, 0.5, f, None) == 3  # fp32 needs 4-byte alignment
+    for bad in (float("inf"), float("nan")):
+        assert lib.fsdp_grad_unscale(u.handle, 0, g, bad, f, None) == 1
+    n = ctypes.c_int64()
+    assert lib.fsdp_grad_sqnorm_workspace(u.handle, -1, ctypes.byref(n)) == 2  # no ALL-ranks form
+    assert lib.fsdp_grad_sqnorm_workspace(u.handle, 0, None) == 1
+    # rank 1 holds 3 elements of the second parameter (and the pad): one tile
+    assert lib.fsdp_grad_sqnorm_workspace(u.handle, 1, ctypes.byref(n)) == 0 and n.value == 1
+    assert lib.fsdp_grad_sqnorm(u.handle, 2, g, w, 8, o, None) == 2
+    assert lib.fsdp_grad_sqnorm(u.handle, 1, g, w, 0, o, None) == 2  # workspace too small
+    assert "needs 1" in B.fsdp_last_error()
+    assert lib.fsdp_grad_sqnorm(u.handle, 1, g, w, 1, None, None) == 1
+    assert lib.fsdp_grad_sqnorm(u.handle, 1, None, w, 1, o, None) == 1
+    assert lib.fsdp_grad_sqnorm(u.handle, 1, g, None, 1, o, None) == 1
+    assert lib.fsdp_grad_sqnorm(u.handle, 1, g, w + 4, 1, o, None) == 3  # doubles need 8-byte alignment
+    e = B.fsdp_unit_create(B.FSDP_FLAT, [], 3)  # empty unit: nothing to do, nothing launched
+    assert lib.fsdp_grad_unscale(e.handle, 0, None, 0.5, None, None) == 0
+    assert lib.fsdp_grad_sqnorm_workspace(e.handle, 0, ctypes.byref(n)) == 0 and n.value == 0
+    assert lib.fsdp_grad_sqnorm(e.handle, 0, None, None, 0, None, None) == 0
