@@ -322,10 +322,13 @@ FSDP_API fsdp_status fsdp_grad_accumulate(const fsdp_unit* unit, int32_t k, cons
  * all-reduce).
  *   grad      : device pointer, fp32, updated in place.
  *   inv_scale : finite.
- *   found_inf : device pointer to one float.
- * Errors: FSDP_E_ARG (NULL unit, grad or found_inf; inv_scale not finite),
- * FSDP_E_RANGE (k), FSDP_E_ALIGN, FSDP_E_HIP.  With no elements (an empty
- * unit) nothing is launched and grad and found_inf may be NULL.
+ *   found_inf : device pointer to one float, or NULL to scale only (the
+ *               clip-coefficient multiply of gradient clipping: after the
+ *               norms of fsdp_grad_sqnorm are combined across ranks, every rank
+ *               scales its shard by the same coefficient).
+ * Errors: FSDP_E_ARG (NULL unit or grad; inv_scale not finite), FSDP_E_RANGE
+ * (k), FSDP_E_ALIGN, FSDP_E_HIP.  With no elements (an empty unit) nothing is
+ * launched and grad may be NULL.
  */
 FSDP_API fsdp_status fsdp_grad_unscale(const fsdp_unit* unit, int32_t k, float* grad,
                                        float inv_scale, float* found_inf, void* stream);

@@ -382,10 +382,11 @@ _F64 = ("torch.float64",)
 
 def fsdp_grad_unscale(unit: Unit, k: int, grad, inv_scale: float, found_inf, stream=None) -> None:
     """grad *= inv_scale over rank k's shard or (FSDP_ALL_RANKS) all L; found_inf (one
-    float) is set to 1 if any input was not finite, never cleared."""
+    float, or None to scale only) is set to 1 if any input was not finite, never cleared."""
     n = unit.L if k == FSDP_ALL_RANKS else unit.S
     _need(grad, n, "grad")
-    _need(found_inf, 1, "found_inf")
+    if found_inf is not None:
+        _need(found_inf, 1, "found_inf")
     _check(load().fsdp_grad_unscale(unit.handle, k, _addr(grad, _F32) or None, inv_scale,
                                     _addr(found_inf, _F32) or None, _stream(stream, grad)))
 

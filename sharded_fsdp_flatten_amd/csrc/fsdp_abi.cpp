@@ -382,7 +382,8 @@ fsdp_status fsdp_grad_unscale(const fsdp_unit* unit, int32_t k, float* grad, flo
     const int64_t n = k == FSDP_ALL_RANKS ? u.L : u.S;
     if ((s = check_buf(grad, n, sizeof(float), "grad")) != FSDP_OK) return s;
     if (n == 0) return ok();
-    if ((s = check_buf(found_inf, 1, sizeof(float), "found_inf")) != FSDP_OK) return s;
+    if (found_inf && !aligned_to(found_inf, sizeof(float)))
+        return fail(FSDP_E_ALIGN, "found_inf is not aligned to its element size");
     const hipError_t e = fsdp::launch_grad_unscale(grad, n, inv_scale, found_inf,
                                                    static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "fsdp_grad_unscale launch");

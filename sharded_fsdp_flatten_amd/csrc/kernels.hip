@@ -796,7 +796,7 @@ void launch_reduce_mode(const ReduceArgs& a, bool hybrid, bool accum, dim3 grid,
 // ---------------------------------------------------------------------------
 // In place: plain loads and nt stores (as AdamW).  A wave that saw a non-finite
 // input has one lane store 1.0f into the flag (vector store; every writer stores
-// the same value, so concurrent stores agree).
+// the same value, so concurrent stores agree).  found == nullptr: scaling only.
 template <bool kVec>
 __global__ __launch_bounds__(kThreads) void unscale_kernel(float* __restrict__ g, int64_t len,
                                                            float inv, float* __restrict__ found) {
@@ -828,6 +828,7 @@ __global__ __launch_bounds__(kThreads) void unscale_kernel(float* __restrict__ g
             }
         }
     }
+    if (found == nullptr) return;  // scaling only (uniform)
     const uint64_t mask = __ballot(bad);
     if (mask != 0 && (threadIdx.x & 63) == static_cast<unsigned>(__builtin_ctzll(mask))) *found = 1.0f;
 }

@@ -419,7 +419,7 @@ def test_unscale_and_sqnorm_errors(B):
     assert lib.fsdp_grad_unscale(None, 0, g, 0.5, f, None) == 1
     assert lib.fsdp_grad_unscale(u.handle, 2, g, 0.5, f, None) == 2
     assert lib.fsdp_grad_unscale(u.handle, 0, None, 0.5, f, None) == 1
-    assert lib.fsdp_grad_unscale(u.handle, 0, g, 0.5, None, None) == 1
+    assert lib.fsdp_grad_unscale(u.handle, 0, g, 0.5, f + 2, None) == 3  # flag must be float-aligned
     assert lib.fsdp_grad_unscale(u.handle, 0, g + 2, 0.5, f, None) == 3  # fp32 needs 4-byte alignment
     for bad in (float("inf"), float("nan")):
         assert lib.fsdp_grad_unscale(u.handle, 0, g, bad, f, None) == 1

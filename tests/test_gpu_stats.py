@@ -92,6 +92,22 @@ def test_unscale_flags_non_finite_inputs_and_shares_the_flag(mis):
         assert to_host(flag)[0] == (0.0 if i == 0 else 1.0)
 
 
+@pytest.mark.parametrize("n,mis", [(4096 * 5 + 3, 0), (777, 1)])
+def test_scale_without_flag_is_the_same_multiply(n, mis):
+    """found_inf NULL: the clip-coefficient multiply; non-finite values pass through."""
+    host = _grads(n, 9)
+    host[3] = np.inf
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(n,)], 1)
+    g, base = offset_view(n, torch.float32, mis)
+    g.copy_(to_dev(host))
+    coef = float(np.float32(0.123456))
+    B.fsdp_grad_unscale(u, 0, g, coef, None)
+    _sync()
+    want = host.copy()
+    oracle.grad_unscale(want, coef, np.zeros(1, np.float32))
+    assert_f32_bits(to_host(g), want, "scale only n=%d" % n)
+
+
 def test_unscale_whole_t5_layout_and_one_rank():
     unit = W.t5_11b_block(N=8)
     u = B.fsdp_unit_create(B.FSDP_FLAT, unit.shapes, 8)
@@ -168,8 +184,9 @@ def test_sqnorm_integer_grads_bit_exact_every_rank(name):
     rng = np.random.Generator(np.random.PCG64(len(name) * 31 + N))
     for k in range(N):
         host = rng.integers(-1024, 1025, u.S).astype(np.float32)
-        host[u.info(k)["valid"]:] = 1e30 if layout == B.FSDP_FLAT else host[u.info(k)["valid"]:]
-        if layout == B.FSDP_ROWS:
+        if layout == B.FSDP_FLAT:
+            host[u.info(k)["valid"]:] = 1e30  # padding sits at the end of the shard
+        else:
             q = 0
             for s in shapes:
                 m, r = oracle.rows_of(s)
