@@ -11,24 +11,30 @@
 //     (a grid-stride version of the same copy runs ~20% slower);
 //   - outputs stored non-temporally (streamed, never re-read by the kernel).
 // The kernels:
-//   - segcopy: one engine for flatten (FSDP1 and FSDP2) and copy-out.  The host
-//     planner turns the layout into a short table of (src, dst, length[, block
-//     stride]) segments passed in the kernel argument block; each workgroup
-//     takes one tile of one segment (the tile -> segment lookup is a
-//     wave-uniform binary search on scalar registers), so no lane ever searches
-//     and every tile is a straight streaming copy.  When a segment's source and
-//     destination are not 16-byte co-aligned, the tile is staged through LDS
-//     and re-read at the element shift, so HBM still sees only aligned vector
-//     loads and stores.
-//   - grad_reduce: each lane owns 8 consecutive outputs, loads 8 bf16 of 8
-//     ranks at a time (128-bit each) before adding them in rank order.
+//   - segcopy: one engine for flatten (FSDP1 and FSDP2), copy-out, the cast and
+//     the bf16 copies.  The host planner turns the layout into a short table of
+//     (src, dst, length[, block stride]) segments passed in the kernel argument
+//     block; each workgroup takes one tile of one segment (the tile -> segment
+//     lookup is a wave-uniform binary search on scalar registers), so no lane
+//     ever searches and every tile is a straight streaming copy.  When source
+//     and destination are not 16-byte co-aligned, a scalar head aligns the
+//     destination and the source is read in place with dword-aligned 16-byte
+//     loads; only a bf16 source at an odd element offset is staged through LDS.
+//   - grad_reduce: each lane owns 8 consecutive outputs and loads their 8 bf16
+//     from 8 ranks at a time (one 16-byte load each, or a shifted pair when a
+//     contribution is only 2-byte aligned) before adding them in rank order;
+//     whole tiles swap halves across lanes so each store writes 1 KiB; the tile
+//     the output's end cuts runs first, its last len % 8 outputs one per lane.
 //   - adamw: elementwise over 8 elements per lane, 128-bit loads and stores.
 //     Its state is read and written back in place: plain loads measure faster
 //     than nt ones (6.5 vs 5.6 TB/s), and nt stores put its writes in HBM within
 //     its own launch (plain stores leave them dirty in the 256 MB Infinity Cache,
 //     which costs the next kernels, or AdamW itself once they outgrow it).
-// Every floating-point step is one IEEE binary32 operation, in the order the
-// CPU oracle fixes; contraction into FMA is disabled for this file.
+//   - accumulate, unscale: elementwise in place, four 16-byte vectors per lane.
+//   - sqnorm: per-parameter sums of squares in binary64, one tile per workgroup
+//     into a workspace, then one workgroup per parameter, in fixed orders.
+// Every binary32 step is one IEEE operation, in the order the CPU oracle fixes;
+// contraction into FMA is disabled for this file.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -147,7 +153,7 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
 
 // Element pipes of the copy engine.  A vector is one 16-byte source load (4 fp32
 // or 8 bf16) and one store of the same element count (16 bytes, or 8 bytes for
-// fp32 -> bf16).  kVpl vectors per lane make a tile of kThreads * E * kVpl
+// fp32 -> bf16); `gather` re-reads a bf16 vector from LDS at an element shift.  kVpl vectors per lane make a tile of kThreads * E * kVpl
 // elements, lane l owning vectors l, l + kThreads, ... so every load and store
 // instruction is contiguous across the wave.
 template <typename SrcT, typename DstT> struct Cp;
@@ -157,7 +163,6 @@ template <> struct Cp<float, float> {
     using V = f4;
     __device__ static V load(const float* p) { return ld4(p); }
     __device__ static V loadw(const float* p) { return ld4w(p); }
-    __device__ static V gather(const float* p) { return f4{p[0], p[1], p[2], p[3]}; }
     __device__ static void put(float* d, V x) { st4(d, x); }
     __device__ static void put1(float* d, float x) { *d = x; }
     __device__ static void zero(float* d) { st4(d, f4{0.0f, 0.0f, 0.0f, 0.0f}); }
@@ -169,7 +174,6 @@ template <> struct Cp<float, uint16_t> {
     using V = f4;
     __device__ static V load(const float* p) { return ld4(p); }
     __device__ static V loadw(const float* p) { return ld4w(p); }
-    __device__ static V gather(const float* p) { return f4{p[0], p[1], p[2], p[3]}; }
     __device__ static void put(uint16_t* d, V x) {
         stu2(d, u2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
     }
@@ -273,19 +277,23 @@ __device__ __forceinline__ void tile_general(const SrcT* s, DstT* d, int n, SrcT
         tile_aligned<SrcT, DstT>(s, d, n);
         return;
     }
-    if (sizeof(SrcT) >= 4 || (shift & 1) == 0) {  // tile-uniform
+    if constexpr (sizeof(SrcT) >= 4) {
         tile_aligned<SrcT, DstT, true>(s, d, n);
-        return;
+    } else {
+        if ((shift & 1) == 0) {  // tile-uniform
+            tile_aligned<SrcT, DstT, true>(s, d, n);
+            return;
+        }
+        const SrcT* base = s - shift;
+        const int nload = (shift + n + E - 1) / E;  // <= tile/E + 1 vectors
+        for (int v = threadIdx.x; v < nload; v += kThreads)
+            *reinterpret_cast<typename P::V*>(lds + E * v) = P::load(base + E * v);
+        __syncthreads();
+        const int nv = n / E;
+        for (int v = threadIdx.x; v < nv; v += kThreads) P::put(d + E * v, P::gather(lds + shift + E * v));
+        for (int e = E * nv + threadIdx.x; e < n; e += kThreads) P::put1(d + e, lds[shift + e]);
+        __syncthreads();
     }
-    const SrcT* base = s - shift;
-    const int nload = (shift + n + E - 1) / E;  // <= tile/E + 1 vectors
-    for (int v = threadIdx.x; v < nload; v += kThreads)
-        *reinterpret_cast<typename P::V*>(lds + E * v) = P::load(base + E * v);
-    __syncthreads();
-    const int nv = n / E;
-    for (int v = threadIdx.x; v < nv; v += kThreads) P::put(d + E * v, P::gather(lds + shift + E * v));
-    for (int e = E * nv + threadIdx.x; e < n; e += kThreads) P::put1(d + e, lds[shift + e]);
-    __syncthreads();
 }
 
 // One tile per workgroup (grid = number of tiles).
@@ -333,9 +341,7 @@ struct ReduceArgs {
     int32_t group;       // hybrid: ranks per group (the launch holds whole groups)
     int32_t first;       // the sum starts in this launch (else out holds the partial)
     int32_t last;        // this launch divides by post (and accumulates)
-    int32_t unused0;     // (accumulation is a template parameter of the kernel)
-    int32_t unused;
-    float pre, rpre, post, unused2;
+    float pre, rpre, post;
 };
 
 // One term: a bf16 (already in the upper half of `bits`) widened exactly, then
