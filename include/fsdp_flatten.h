@@ -143,9 +143,10 @@ FSDP_API const char* fsdp_status_string(int32_t status);
  * [0, FSDP_MAX_NDIM] dimensions, taken in order from `dims` (so `dims` holds
  * sum(ndims) entries, each >= 0).  N >= 1.  On success *out receives a handle
  * that the caller frees with fsdp_unit_destroy.  Allocates host memory only;
- * makes no HIP call.  Errors: FSDP_E_ARG (null out, or null ndims/dims with
- * n_params > 0), FSDP_E_RANGE (layout, N, n_params, a dim or ndim out of
- * range), FSDP_E_OVERFLOW (a size beyond int64), FSDP_E_NOMEM.
+ * makes no HIP call.  Errors: FSDP_E_ARG (null out, null ndims with
+ * n_params > 0, or null dims when sum(ndims) > 0), FSDP_E_RANGE (layout, N,
+ * n_params, a dim or ndim out of range), FSDP_E_OVERFLOW (a size beyond
+ * int64), FSDP_E_NOMEM.
  */
 FSDP_API fsdp_status fsdp_unit_create(int32_t layout, int32_t n_params, const int32_t* ndims,
                              const int64_t* dims, int32_t N, fsdp_unit** out);

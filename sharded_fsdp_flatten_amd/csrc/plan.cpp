@@ -65,8 +65,14 @@ int plan_create(int32_t layout, int32_t n_params, const int32_t* ndims, const in
         *err = "n_params must be >= 0";
         return kRange;
     }
-    if (n_params > 0 && (!ndims || !dims)) {
-        *err = "ndims and dims must not be NULL when n_params > 0";
+    if (n_params > 0 && !ndims) {
+        *err = "ndims must not be NULL when n_params > 0";
+        return kArg;
+    }
+    int64_t total_dims = 0;  // dims holds sum(ndims) entries; it may be NULL when that is 0
+    for (int32_t i = 0; i < n_params; ++i) total_dims += ndims[i] > 0 ? ndims[i] : 0;
+    if (total_dims > 0 && !dims) {
+        *err = "dims must not be NULL when some parameter has dimensions";
         return kArg;
     }
     UnitPlan u;

@@ -174,6 +174,12 @@ def test_create_errors(B):
     import ctypes
     out = ctypes.c_void_p()
     assert lib.fsdp_unit_create(1, 2, None, None, 1, ctypes.byref(out)) == 1  # null tables
+    # only scalars: sum(ndims) = 0, so dims may be NULL; a NULL dims with dimensions may not
+    nd0 = (ctypes.c_int32 * 2)(0, 0)
+    assert lib.fsdp_unit_create(1, 2, nd0, None, 3, ctypes.byref(out)) == 0
+    lib.fsdp_unit_destroy(out)
+    nd1 = (ctypes.c_int32 * 2)(0, 1)
+    assert lib.fsdp_unit_create(1, 2, nd1, None, 3, ctypes.byref(out)) == 1
 
 
 def test_info_and_offset_errors(B):
