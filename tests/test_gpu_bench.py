@@ -23,7 +23,8 @@ def _run(*args, timeout=240):
 
 
 def test_bench_json_line_on_the_tiny_unit():
-    p = _run("--workload", "tiny", "--steps", "5", "--warmup", "1", "--next", "--sweep-ranks")
+    p = _run("--workload", "tiny", "--steps", "5", "--warmup", "1", "--next", "--sweep-ranks",
+             "--graph", "on")
     assert p.returncode == 0, p.stderr[-2000:]
     lines = [l for l in p.stdout.splitlines() if l.startswith("{")]
     assert len(lines) == 1
@@ -45,6 +46,9 @@ def test_bench_json_line_on_the_tiny_unit():
     for k in pr["ranks"]:
         assert set(pr[str(k)]) == {"grad_reduce", "adamw", "flatten"}
     assert set(pr["worst"]) == {"grad_reduce", "adamw", "flatten"}
+    gr = d["graph"]
+    assert gr["ms_per_step"] > 0 and abs(gr["value"] - step_bytes / (gr["ms_per_step"] * 1e-3) / 1e9) \
+        <= 0.01 * gr["value"] + 0.1
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
@@ -52,3 +56,15 @@ def test_bench_json_line_on_the_tiny_unit():
     assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["sample"]
     assert "copyin_bf16_all_ranks" in d["next_rows"]
 
+
+
+def test_bench_headline_from_graph_replays_without_flush():
+    """Without a flush the step is timed from HIP-graph replays; the eager loop is kept."""
+    p = _run("--workload", "tiny", "--steps", "5", "--warmup", "1", "--flush", "off",
+             "--no-cpu-baseline")
+    assert p.returncode == 0, p.stderr[-2000:]
+    d = json.loads([l for l in p.stdout.splitlines() if l.startswith("{")][0])
+    assert d["config"]["step_time"] == "wall clock of HIP-graph replays of the step"
+    step_bytes = sum(k["bytes"] for k in d["kernels"].values())
+    assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"] + 0.1
+    assert d["eager"]["ms_per_step"] > 0 and "graph" not in d
