@@ -16,6 +16,7 @@ FSDP_FLAT = 1
 FSDP_ROWS = 2
 FSDP_ALL_RANKS = -1
 FSDP_MAX_NDIM = 8
+ABI_VERSION = 2  # FSDP_ABI_VERSION of include/fsdp_flatten.h this binding marshals for
 
 STATUS_NAMES = {0: "FSDP_OK", 1: "FSDP_E_ARG", 2: "FSDP_E_RANGE", 3: "FSDP_E_ALIGN",
                 4: "FSDP_E_OVERFLOW", 5: "FSDP_E_NOMEM", 6: "FSDP_E_HIP",
@@ -70,6 +71,9 @@ def load() -> ctypes.CDLL:
     st = ctypes.c_int32
     lib.fsdp_abi_version.argtypes = []
     lib.fsdp_abi_version.restype = ctypes.c_int32
+    if lib.fsdp_abi_version() != ABI_VERSION:
+        raise RuntimeError("%s implements ABI version %d; this binding needs %d (rebuild it)"
+                           % (LIB_PATH, lib.fsdp_abi_version(), ABI_VERSION))
     lib.fsdp_last_error.argtypes = []
     lib.fsdp_last_error.restype = ctypes.c_char_p
     lib.fsdp_status_string.argtypes = [ctypes.c_int32]

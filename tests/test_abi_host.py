@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(B):
 
 def test_abi_version_matches_header(B):
     v = int(re.search(r"#define FSDP_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
-    assert B.fsdp_abi_version() == v
+    assert B.fsdp_abi_version() == v == B.ABI_VERSION
 
 
 def _labelled(shapes):
