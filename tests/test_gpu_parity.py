@@ -603,3 +603,37 @@ def test_gpt175b_n120_grad_reduce_full(big175):
     del c
     assert_f32_tol_then_bits(to_host(out), oracle.grad_reduce(list(c_host), 8.0, 15.0),
                              "175b N=120 reduce")
+
+
+@pytest.mark.parametrize("layout,name,N", [(B.FSDP_FLAT, "gpt2l", 8), (B.FSDP_FLAT, "tiny", 3),
+                                           (B.FSDP_ROWS, "rows", 8)])
+def test_multi_rank_without_a_cluster(layout, name, N):
+    """N is only a layout parameter: looping k = 0..N-1 on one GPU, the shards concatenate to
+    the all-ranks layout (what an AllGather of them returns), and rank k's reduction of the N
+    simulated ranks' slices [kS, (k+1)S) of their full gradients is slice k of the reduction of
+    the full gradients (what a ReduceScatter returns)."""
+    unit = _unit_by_name(name, N)
+    params = W.host_params(unit, seed=0)
+    u = B.fsdp_unit_create(layout, unit.shapes, N)
+    d_params = [to_dev(p) for p in params]
+    shards = []
+    for k in range(N):
+        out = torch.full((u.S,), float("nan"), device=dev())
+        B.fsdp_flatten_shard(u, d_params, k, out)
+        shards.append(out)
+    whole = torch.full((u.L,), float("nan"), device=dev())
+    B.fsdp_flatten_shard(u, d_params, B.FSDP_ALL_RANKS, whole)
+    _sync()
+    assert torch.equal(torch.cat(shards).view(torch.int32), whole.view(torch.int32))
+    # ReduceScatter: N simulated ranks, each with a full-length bf16 gradient
+    full = W.host_contribs(N, u.L, step=7)
+    d_full = [to_dev(full[r]) for r in range(N)]
+    red = []
+    for k in range(N):
+        grad = torch.full((u.S,), float("nan"), device=dev())
+        B.fsdp_grad_reduce_shard(u, [d_full[r][k * u.S:(k + 1) * u.S] for r in range(N)],
+                                 2.0, N / 2.0, grad)
+        red.append(grad)
+    _sync()
+    assert_f32_bits(to_host(torch.cat(red)), oracle.grad_reduce(list(full), 2.0, N / 2.0),
+                    "%s reduce-scatter over N=%d" % (name, N))
