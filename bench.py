@@ -58,9 +58,12 @@ def parse_args():
                     help="gradient contributions as one receive buffer with rows at the library's "
                          "recommended pitch (S rounded up to whole 128-byte lines; default), as one "
                          "[N, S] buffer with rows S apart, or as N separate allocations")
-    ap.add_argument("--next", action="store_true",
+    ap.add_argument("--next", dest="next", action="store_true", default=True,
                     help="also time the next rows (hybrid + accumulating reduce, bf16 copy-in, "
-                         "cast, bf16 copy-out, local accumulation) in a second cold-cache loop")
+                         "unscale, cast, bf16 copy-out, local accumulation, sums of squares) in a "
+                         "second cold-cache loop (the default)")
+    ap.add_argument("--no-next", dest="next", action="store_false",
+                    help="time the four calls of the step only")
     ap.add_argument("--flush", default="auto", choices=["auto", "on", "off"],
                     help="read 1 GiB before every timed kernel so that nothing it reads can sit in "
                          "the 256 MB Infinity Cache (auto: on when the copy-out moves < 2 GB, where "
