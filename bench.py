@@ -295,7 +295,7 @@ def main():
     args = parse_args()
     if args.gpus != 1:
         print("bench.py measures one rank's share of one FSDP unit on ONE GPU; --gpus %d is not "
-              "supported (no collectives are part of this build)" % args.gpus, file=sys.stderr)
+              "supported (the library has no collectives: it measures one rank's share)" % args.gpus, file=sys.stderr)
         return 2
 
     import numpy as np

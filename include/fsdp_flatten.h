@@ -64,7 +64,7 @@ typedef enum {
     FSDP_E_OVERFLOW = 4,     /* a size overflows int64                        */
     FSDP_E_NOMEM = 5,        /* host allocation of the unit plan failed       */
     FSDP_E_HIP = 6,          /* a HIP runtime call or kernel launch failed    */
-    FSDP_E_UNSUPPORTED = 7   /* valid request this build does not handle      */
+    FSDP_E_UNSUPPORTED = 7   /* valid request the library does not handle     */
 } fsdp_status;
 
 /* How a unit is sharded. */
