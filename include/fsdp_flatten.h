@@ -29,9 +29,12 @@
  *     inside kernels surface at the caller's next synchronisation, as for any
  *     HIP work.  fsdp_last_error() returns a message for the calling thread's
  *     last non-OK status.
- *   - Pointer alignment is not an error: 16-byte-aligned operands take the
- *     128-bit vector path, anything else (4-byte fp32 / 2-byte bf16 aligned)
- *     the realigning path.  Misaligned below the element size is FSDP_E_ALIGN.
+ *   - Pointer alignment is not an error: data at least 4-byte aligned is read
+ *     with 16-byte loads where it sits (a scalar head first aligns outputs),
+ *     and bf16 data at odd element offsets is realigned in the kernels.
+ *     Misaligned below the element size is FSDP_E_ALIGN.
+ *   - No call allocates, synchronises or records a memset, so every call can
+ *     be captured in a HIP graph and replayed.
  *   - Inputs and outputs must not overlap, except that fsdp_adam_shard updates
  *     param, exp_avg and exp_avg_sq in place.
  *   - A unit with no elements makes every call a no-op that returns FSDP_OK.
