@@ -253,7 +253,7 @@ FSDP_API fsdp_status fsdp_adam_shard(const fsdp_unit* unit, float* param, const 
  * layout (L elements).  The pages cast the full-precision shard to low
  * precision once per FlatParameter and all-gather the low-precision copy
  * ([P1] section 3.4, "Native Mixed Precision and the Sharded Gradient Scaler";
- * [P2] section 5: FSDP2 all-gathers bf16 parameters); the same cast turns an
+ * [P2] section 5: FSDP2 gathers the bf16 copy); the same cast turns an
  * fp32-accumulated gradient into the bf16 ReduceScatter input.
  *   src : device pointer, fp32.   dst : device pointer, bf16 (same count).
  */
@@ -345,7 +345,7 @@ FSDP_API fsdp_status fsdp_grad_sqnorm_workspace(const fsdp_unit* unit, int32_t k
 /*
  * Per-parameter sums of squares of rank k's gradient shard.  The pages note
  * that statistics of original parameters (gradient-clipping norms, per-
- * parameter optimizer statistics) "become invalid" on flat shards, which
+ * parameter optimizer statistics) are wrong when taken over flat shards, which
  * ignore parameter boundaries ([P1] section 6, the mathematical-equivalence
  * limitation).  The unit plan knows the boundaries, so
  *   out[i] = sum of grad[j]^2 over the shard elements of parameter i

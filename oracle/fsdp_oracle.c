@@ -81,7 +81,7 @@ void orc_bf16_array(int64_t n, const float* x, uint16_t* y) {
  * Sizes of a FlatParameter over N ranks ([P1] §3.4 "FlatParameter:
  * Flattening, Concatenation, and Sharding"): the unit's parameters are
  * flattened and concatenated (T elements), padded on the right so that the
- * length is divisible by the sharding factor (pad <= N-1), and cut into N
+ * length is a multiple of N (pad <= N-1), and cut into N
  * equal chunks of S elements.
  * out[0]=T, out[1]=S, out[2]=L=N*S, out[3]=pad=L-T.
  */
@@ -315,7 +315,7 @@ void orc_adamw(int64_t len, float* p, const float* g, float* m, float* v, double
  * The same FlatParameter and FSDP2 layouts as above, for 16-bit elements:
  * casting before the AllGather moves bf16 parameters ([P1] section 3.4,
  * "Native Mixed Precision": collectives in low precision; [P2] section 5:
- * FSDP2 all-gathers bf16 parameters), and the ReduceScatter input is the
+ * the bf16 copy is what FSDP2 gathers), and the ReduceScatter input is the
  * unsharded bf16 gradient laid out like the FlatParameter ([P1] section 3.4,
  * "Communication layout").  Padding is the bit pattern 0x0000 (+0.0).
  */
@@ -387,8 +387,8 @@ void orc_rows_copyout_u16(int32_t p, const int64_t* m, const int64_t* r, int64_t
 /* ------------------------------------------------------------------------ */
 
 /*
- * Hybrid sharding ([P1] section 3.4, "Sharding Strategies", the sum over all
- * W ranks equals the sum over the W/F sharding groups of the in-group sums):
+ * Hybrid sharding ([P1] section 3.4, "Sharding Strategies": summing the W/F
+ * sharding groups' in-group totals gives the total over every rank):
  * the N ranks form N/F groups of F consecutive ranks; each group's terms are
  * summed first (the ReduceScatter inside the sharding group), then the group
  * sums (the AllReduce across replicas).  Reading taken for the order: both
@@ -462,8 +462,8 @@ void orc_grad_unscale(int64_t n, float* g, float inv_scale, float* found_inf) {
 /*
  * Per-parameter sums of squares of rank k's FLAT gradient shard.  The pages
  * warn that statistics of original parameters (norms for gradient clipping,
- * per-parameter optimizer statistics) "become invalid" when computed on flat
- * shards, because a shard ignores parameter boundaries ([P1] section 6
+ * per-parameter optimizer statistics) are no longer correct when computed on
+ * flat shards, because a shard ignores parameter boundaries ([P1] section 6
  * "Limitations", the mathematical-equivalence caveat).  The unit's layout
  * knows the boundaries: every shard element [kS, (k+1)S) of the flat buffer is
  * attributed to the parameter it came from (padding to none), and

@@ -46,7 +46,7 @@ def test_mean_of_equal_contributions_is_exact(orc, N):
 
 
 def test_integer_contributions_sum_exactly_and_decompose(orc):
-    """Integer-valued terms sum exactly in fp32; so the sum over all W ranks equals the sum
+    """Integer-valued terms sum exactly in fp32; so the total of the W ranks' terms equals the sum
     over W/F sharding groups of the in-group sums (hybrid sharding decomposition)."""
     rng = np.random.Generator(np.random.PCG64(8))
     Wn, F, n = 32, 8, 4096

@@ -1,6 +1,6 @@
 """Pins of the oracle's FSDP2 per-parameter dim-0 sharding.
 
-The pages fix: every parameter is chunked on dim 0 with torch.chunk ("FSDP"
+The pages fix: torch.chunk splits each parameter along dim 0 ("FSDP"
 concept page, FSDP1 vs FSDP2), each rank holding complete rows ("FSDP Under The
 Hood", section 2).  torch.chunk itself is the library routine checked against.
 """
