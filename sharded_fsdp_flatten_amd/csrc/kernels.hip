@@ -25,6 +25,9 @@
 //     contribution is only 2-byte aligned) before adding them in rank order;
 //     whole tiles swap halves across lanes so each store writes 1 KiB; the tile
 //     the output's end cuts runs first, its last len % 8 outputs one per lane.
+//     From 32 ranks and 12,288 whole tiles on, a row-major sweep instead: each
+//     wave holds 16 tiles' sums and walks the ranks in order, the grid sized to be
+//     resident at once, so HBM serves a few contribution rows at a time.
 //   - adamw: elementwise over 8 elements per lane, 128-bit loads and stores.
 //     Its state is read and written back in place: plain loads measure faster
 //     than nt ones (6.5 vs 5.6 TB/s), and nt stores put its writes in HBM within
@@ -38,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
 #include <cmath>
 #include <vector>
@@ -72,6 +76,15 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #endif
 #ifndef FSDP_REDUCE_AHEAD
 #define FSDP_REDUCE_AHEAD 8
+#endif
+#ifndef FSDP_SWEEP_MIN_RANKS
+#define FSDP_SWEEP_MIN_RANKS 32  // the reduction sweeps ranks row-major from this many on
+#endif
+#ifndef FSDP_SWEEP_V
+#define FSDP_SWEEP_V 16          // whole tiles a sweep wave holds (8, 12, 16: 6.23, 6.36, 6.53 TB/s)
+#endif
+#ifndef FSDP_SWEEP_MIN_TILES
+#define FSDP_SWEEP_MIN_TILES 12288  // and from this many whole 512-output tiles on
 #endif
 #ifndef FSDP_ACC_VPL
 #define FSDP_ACC_VPL 4          // 4-element vectors per lane in the local accumulation (1/2/4: 5.70/5.96/6.07 TB/s)
@@ -488,10 +501,28 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
     a.out[j] = acc;
 }
 
+// Stores a wave's 512 outputs of one whole tile, lane l holding outputs 8l .. 8l+7
+// in acc: the halves are swapped across lanes (ds_bpermute, no LDS allocation) so
+// that each store instruction writes 1 KiB of whole cache lines.  lane l stores
+// outputs 4l .. 4l+3 of each 256-output half, which lane 32h + l/2 holds.
+__device__ __forceinline__ void store_whole8(float* wave_out, const float* acc) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int src = 32 * h + (lane >> 1);
+        float w[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float lo = __shfl(acc[i], src, 64);
+            const float hi = __shfl(acc[4 + i], src, 64);
+            w[i] = (lane & 1) ? hi : lo;
+        }
+        st4(wave_out + 256 * h + 4 * lane, f4{w[0], w[1], w[2], w[3]});
+    }
+}
+
 // The 8 outputs j0 .. j0+7 of one lane over this launch's ranks.  kWhole: the tile
-// is whole, and its halves are swapped across lanes (ds_bpermute, no LDS
-// allocation) so that each store instruction writes 1 KiB of whole cache lines;
-// otherwise each lane stores its own 8.
+// is whole and is stored with store_whole8; otherwise each lane stores its own 8.
 template <int kPre, int kLd, bool kHybrid, bool kAccum, bool kWhole>
 __device__ __forceinline__ void reduce_lane(const ReduceArgs& a, int64_t j0) {
     constexpr int kEpt = 8;
@@ -545,22 +576,7 @@ __device__ __forceinline__ void reduce_lane(const ReduceArgs& a, int64_t j0) {
         }
     }
     if constexpr (kWhole) {
-        // lane l stores outputs 4l..4l+3 of each 256-output half of its wave's 512,
-        // which lane 32h + l/2 holds
-        const int lane = threadIdx.x & 63;
-        float* wave_out = a.out + (j0 - 8 * lane);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int src = 32 * h + (lane >> 1);
-            float w[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float lo = __shfl(acc[i], src, 64);
-                const float hi = __shfl(acc[4 + i], src, 64);
-                w[i] = (lane & 1) ? hi : lo;
-            }
-            st4(wave_out + 256 * h + 4 * lane, f4{w[0], w[1], w[2], w[3]});
-        }
+        store_whole8(a.out + (j0 - 8 * static_cast<int64_t>(threadIdx.x & 63)), acc);
     } else {
         st4(a.out + j0, f4{acc[0], acc[1], acc[2], acc[3]});
         st4(a.out + j0 + 4, f4{acc[4], acc[5], acc[6], acc[7]});
@@ -599,6 +615,103 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
             if (j < a.len) reduce_one<kPre, kHybrid, kAccum>(a, j);
         }
     }
+}
+
+// Many ranks: a row-major sweep.  A tile kernel wave reads 1 KiB from every rank for
+// its 512 outputs, so the waves in flight read from all ranks' rows at once (128
+// contribution rows on a 128-rank shard), and HBM serves that many scattered streams
+// more slowly than a few (read-only: 6.5 against 7.0 TB/s).  Here each wave owns kV
+// consecutive whole tiles (8 kV accumulators per lane) and walks the ranks in order,
+// loading rank r + 1's kV vectors while it adds rank r's; the host sizes the grid so
+// that every wave is resident at once, so the waves move through the ranks together
+// and HBM serves a few rows at a time.  Per output the operations and their order are
+// those of the tile path (flat sum, whole-dword contributions), so the results are
+// identical.  Block layout of a launch: the tile the output's end cuts (if any), then
+// n_single whole tiles that take the tile path, then the sweep waves.
+struct SweepArgs {
+    ReduceArgs r;
+    int64_t t_first;   // first whole tile (512 outputs) of this launch
+    int32_t cut;       // 1: block 0 reduces the tile the output's end cuts
+    int32_t n_single;  // then this many blocks reduce one whole tile each
+};
+
+template <int kPre, bool kAccum, int kV>
+__device__ __forceinline__ void sweep_wave(const ReduceArgs& a, int64_t t0) {
+    constexpr int kTile = 512;
+    const int lane = threadIdx.x & 63;
+    // element offset of the lane's first vector from the run's start (vector v: + 512 v)
+    const int64_t base = t0 * kTile;
+    const int off = 8 * lane;
+    float acc[kV][8];
+    if (a.first) {
+        // -0 + t == t for every t (a NaN comes out quiet, as the divide by post makes
+        // it anyway), so adding rank 0 to -0 gives the tile path's first term
+#pragma unroll
+        for (int v = 0; v < kV; ++v)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[v][e] = -0.0f;
+    } else {
+#pragma unroll
+        for (int v = 0; v < kV; ++v) load_out8(acc[v], a.out + base + off + kTile * v);
+    }
+    u4 x[kV];  // rank r's vectors
+    const uint16_t* c0 = a.c[0] + base;
+#pragma unroll
+    for (int v = 0; v < kV; ++v) x[v] = ldu4w(c0 + off + kTile * v);
+    for (int r = 0; r + 1 < a.nc; ++r) {
+        const uint16_t* cn = a.c[r + 1] + base;
+#pragma unroll
+        for (int v = 0; v < kV; ++v) {
+            // one vector at a time, its adds before its reload: no second copy of any
+            // vector is live, so the wave holds 12 kV registers of data
+            add8<kPre>(acc[v], x[v], a);
+            x[v] = ldu4w(cn + off + kTile * v);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < kV; ++v) add8<kPre>(acc[v], x[v], a);
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+        float* o = a.out + base + kTile * v;
+        if (a.last) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[v][e] = acc[v][e] / a.post;
+            if constexpr (kAccum) {
+                float prev[8];
+                load_out8(prev, o + off);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[v][e] = prev[e] + acc[v][e];
+            }
+        }
+        store_whole8(o, acc[v]);
+    }
+}
+
+template <int kPre, bool kAccum, int kV>
+__global__ __launch_bounds__(64) void reduce_sweep_kernel(SweepArgs s) {
+    const ReduceArgs& a = s.r;
+    constexpr int64_t kTile = 512;
+    int64_t b = blockIdx.x;
+    if (s.cut) {
+        if (b == 0) {
+            // the cut tile: lanes with 8 outputs take the vector path, then the last
+            // len % 8 outputs one lane each
+            const int64_t t = a.len / kTile;
+            const int64_t j0 = t * kTile + 8 * static_cast<int64_t>(threadIdx.x);
+            if (j0 + 8 <= a.len) reduce_lane<kPre, kLdWord, false, kAccum, false>(a, j0);
+            const int64_t j = (a.len & ~int64_t{7}) + threadIdx.x;
+            if (j < a.len) reduce_one<kPre, false, kAccum>(a, j);
+            return;
+        }
+        --b;
+    }
+    if (b < s.n_single) {
+        reduce_lane<kPre, kLdWord, false, kAccum, true>(
+            a, (s.t_first + b) * kTile + 8 * static_cast<int64_t>(threadIdx.x));
+        return;
+    }
+    sweep_wave<kPre, kAccum, kV>(a, s.t_first + s.n_single + (b - s.n_single) * kV);
 }
 
 // ---------------------------------------------------------------------------
@@ -936,6 +1049,72 @@ hipError_t launch_segcopy(const std::vector<CopySeg>& segs, Pipe pipe, hipStream
     return hipErrorInvalidValue;
 }
 
+// Workgroups of reduce_sweep_kernel<kPre, kAccum, kSweepV> resident at once on the
+// current device (occupancy per CU times CUs), queried once per device; 0 if unknown.
+constexpr int kSweepV = FSDP_SWEEP_V;
+constexpr int kMaxDevices = 64;
+template <int kPre, bool kAccum>
+int64_t sweep_capacity() {
+    static std::atomic<int64_t> cap[kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+    int64_t c = cap[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(&reduce_sweep_kernel<kPre, kAccum, kSweepV>),
+                64, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        c = int64_t{per_cu} * cus;
+        cap[dev].store(c > 0 ? c : -1, std::memory_order_relaxed);
+    }
+    return c > 0 ? c : 0;
+}
+
+// The sweep over this launch's ranks: the whole tiles are split into as few runs as
+// keep every run's grid (cut tile, fewer than kSweepV single tiles, the waves)
+// resident at once, one launch per run in output order; *err gets the first launch
+// error.  Returns false, having launched nothing, when the output is too short or the
+// occupancy is unknown.
+template <int kPre, bool kAccum>
+bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
+    constexpr int64_t kTile = 512;
+    const int64_t tiles = a.len / kTile;
+    if (tiles < kSweepV || tiles < FSDP_SWEEP_MIN_TILES) return false;
+    const int64_t cap = sweep_capacity<kPre, kAccum>();
+    if (cap <= kSweepV + 1) return false;
+    const int64_t per_run = kSweepV * (cap - kSweepV);  // blocks <= per_run / kV + kV - 1 + 1
+    const int64_t runs = (tiles + per_run - 1) / per_run;
+    const int64_t each = (tiles + runs - 1) / runs;
+    for (int64_t t = 0; t < tiles; t += each) {
+        const int64_t n = std::min(each, tiles - t);
+        SweepArgs s{};
+        s.r = a;
+        s.t_first = t;
+        s.cut = t + n == tiles && a.len % kTile != 0;
+        s.n_single = static_cast<int32_t>(n % kSweepV);
+        const int64_t blocks = s.cut + s.n_single + n / kSweepV;
+        hipLaunchKernelGGL((reduce_sweep_kernel<kPre, kAccum, kSweepV>),
+                           dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream, s);
+        *err = hipGetLastError();
+        if (*err != hipSuccess) break;
+    }
+    return true;
+}
+
+// The sweep, for a flat sum over at least FSDP_SWEEP_MIN_RANKS contributions that are all
+// at least 4-byte aligned into a 16-byte-aligned output; false if it does not apply.
+bool launch_reduce_sweep(const ReduceArgs& a, int mode, bool accum, hipStream_t stream,
+                         hipError_t* err) {
+    if (a.nc < FSDP_SWEEP_MIN_RANKS) return false;
+    if (mode == kPreNone)
+        return accum ? try_sweep<kPreNone, true>(a, stream, err) : try_sweep<kPreNone, false>(a, stream, err);
+    if (mode == kPreRecip)
+        return accum ? try_sweep<kPreRecip, true>(a, stream, err) : try_sweep<kPreRecip, false>(a, stream, err);
+    return accum ? try_sweep<kPreDiv, true>(a, stream, err) : try_sweep<kPreDiv, false>(a, stream, err);
+}
+
 hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib, int64_t len,
                               float pre, float post, int64_t group, bool accumulate, float* out,
                               hipStream_t stream) {
@@ -978,6 +1157,11 @@ hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib
         a.rpre = rpre;
         a.post = post;
         const dim3 grid = grid_of(blocks);
+        hipError_t swept = hipSuccess;
+        if (!hybrid && ld == kLdWord && launch_reduce_sweep(a, mode, accumulate, stream, &swept)) {
+            if (swept != hipSuccess) return swept;
+            continue;
+        }
         if (mode == kPreNone) {
             if (ld == kLdWord) launch_reduce_mode<kPreNone, kLdWord>(a, hybrid, accumulate, grid, stream);
             else if (ld == kLdHalf) launch_reduce_mode<kPreNone, kLdHalf>(a, hybrid, accumulate, grid, stream);

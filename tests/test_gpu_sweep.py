@@ -1,0 +1,134 @@
+"""The gradient reduction's row-major sweep, the path a flat sum takes over at least 32
+contributions that are all 4-byte aligned, into a 16-byte-aligned output of at least 12,288
+whole 512-element tiles.  Parity with the oracle element by element: the tile the output's
+end cuts and the single tiles before the sweep waves, outputs long enough to be split into
+several runs, launches chained over more than 128 ranks (sweep after sweep, tile kernel after
+sweep), accumulation, the three kinds of pre-divide (none, an exact reciprocal, a true
+division) and special values, among them columns that are -0 in every rank (the sweep starts
+its sums from -0, which must leave -0 + -0 + ... = -0)."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from gpu_util import assert_f32_tol_then_bits, dev, to_dev, to_host
+from sharded_fsdp_flatten_amd import binding as B
+
+pytestmark = pytest.mark.gpu
+
+TILE = 512
+MIN_TILES = 12288  # the shortest output (in whole tiles) the sweep takes
+
+
+@pytest.fixture(autouse=True)
+def _free():
+    B.load()
+    yield
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _contribs(N, S, step):
+    """Pitched device rows (the library's recommended receive layout) and their host copy."""
+    pitch = -(-S // 64) * 64
+    c = W.device_contribs(N, S, step=step, pitch=pitch)
+    return c, to_host(c)
+
+
+def _reduce(u, c, pre, post, out=None, accumulate=False):
+    S = c.shape[1]
+    if out is None:
+        out = torch.full((S,), float("nan"), device=dev())
+    rows = [c[r] for r in range(c.shape[0])]
+    if accumulate:
+        B.fsdp_grad_reduce_shard_ex(u, rows, pre, post, out, accumulate=True)
+    else:
+        B.fsdp_grad_reduce_shard(u, rows, pre, post, out)
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("N,tiles,tail,pre,post", [
+    (32, MIN_TILES, 0, 2.0, 16.0),          # exact multiple of 16 tiles: sweep waves only
+    (32, MIN_TILES, 517, 4.0, 8.0),         # plus a cut tile (517 = 64 * 8 + 5)
+    (48, 13000, 7, 3.0, 16.0),              # 8 single tiles, a cut tile of 7, true division
+    (64, 12345, 300, 1.0, 64.0),            # 9 single tiles, no pre-divide
+    (33, 12290, 511, -8.0, 4.125),          # negative power-of-two pre, non-power post
+    (128, 27650, 224, 8.0, 16.0),           # the GPT-175B shard length at 128 ranks
+])
+def test_sweep_reduce(N, tiles, tail, pre, post):
+    S = tiles * TILE + tail
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    assert u.S == S
+    c, ch = _contribs(N, S, step=3)
+    out = _reduce(u, c, pre, post)
+    assert_f32_tol_then_bits(to_host(out), oracle.grad_reduce(list(ch), pre, post),
+                             "sweep N=%d S=%d pre=%g post=%g" % (N, S, pre, post))
+
+
+def test_sweep_split_into_runs():
+    """65,029 whole tiles cannot all be resident at once (16 tiles per wave), so the output
+    is reduced in several runs, one launch each, the last with the cut tile."""
+    N, S = 32, 65029 * TILE + 77
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    c, ch = _contribs(N, S, step=4)
+    out = _reduce(u, c, 2.0, 16.0)
+    assert_f32_tol_then_bits(to_host(out), oracle.grad_reduce(list(ch), 2.0, 16.0),
+                             "sweep in runs S=%d" % S)
+
+
+@pytest.mark.parametrize("N", [160, 130, 300])
+def test_sweep_chained_over_more_than_128_ranks(N):
+    """160 = 128 + 32 (two sweeps), 130 = 128 + 2 (a sweep, then the tile kernel continues
+    from the partial sums), 300 = 128 + 128 + 44 (a middle launch neither first nor last)."""
+    S = MIN_TILES * TILE + 1000
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    c, ch = _contribs(N, S, step=5)
+    pre = 8.0 if N != 300 else 3.0
+    out = _reduce(u, c, pre, N / pre)
+    assert_f32_tol_then_bits(to_host(out), oracle.grad_reduce(list(ch), pre, N / pre),
+                             "chained N=%d" % N)
+
+
+def test_sweep_accumulate():
+    N, S = 64, (MIN_TILES + 5) * TILE + 33
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    old = W.host_normal(S, 1e-3, seed=21)
+    acc = to_dev(old)
+    for t, (pre, post) in enumerate([(8.0, 8.0), (3.0, 7.0)]):
+        c, ch = _contribs(N, S, step=30 + t)
+        _reduce(u, c, pre, post, out=acc, accumulate=True)
+        oracle.grad_reduce_ex(list(ch), pre, post, out=old)
+        assert_f32_tol_then_bits(to_host(acc), old, "sweep accumulate step %d" % t)
+        del c, ch
+
+
+@pytest.mark.parametrize("pre,post", [(1.0, 1.0), (4.0, 8.0), (3.0, 5.0)])
+def test_sweep_special_values(pre, post):
+    N, S = 32, MIN_TILES * TILE + 9
+    rng = np.random.Generator(np.random.PCG64(22))
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    c, ch = _contribs(N, S, step=6)
+    ch = ch.copy()
+    # scattered specials: +-0, +-inf, quiet NaN, the smallest subnormals, +-max finite
+    specials = np.asarray([0x8000, 0x0000, 0x7F80, 0xFF80, 0x7FC0, 0x0001, 0x8001, 0x7F7F,
+                           0xFF7F], np.uint16)
+    for r in range(N):
+        idx = rng.integers(0, S, size=2000)
+        ch[r, idx] = rng.choice(specials, size=idx.size)
+    # then columns -0 in every rank, in a sweep wave's tiles and in the cut tile
+    zero_cols = (0, 4096 * TILE + 3, S - 9)
+    for lo in zero_cols:
+        ch[:, lo:lo + 9] = 0x8000
+    # subnormal in every rank: the pre-divide of a subnormal term
+    ch[:, 100:140] = 0x0001
+    c.copy_(to_dev(ch))
+    out = _reduce(u, c, pre, post)
+    got = to_host(out)
+    want = oracle.grad_reduce(list(ch), pre, post)
+    assert_f32_tol_then_bits(got, want, "sweep specials pre=%g post=%g" % (pre, post))
+    for lo in zero_cols:
+        assert np.all(got[lo:lo + 9].view(np.uint32) == 0x80000000), "-0 column at %d" % lo
