@@ -170,9 +170,11 @@ FSDP_API fsdp_status fsdp_unit_param_offset(const fsdp_unit* unit, int32_t i, in
  * receives the N gradient contributions of fsdp_grad_reduce_shard (row r holds
  * contribution r in its first S elements): S rounded up to a whole 128-byte
  * line (a multiple of 64 elements).  The reduction reads each contribution in
- * 1 KiB runs; rows that start mid-line make every run of theirs touch one more
- * line (at N = 128 on the GPT-175B block, 6.25% more HBM reads and a 6% slower
- * reduction than line-aligned rows).  Any layout works; this one is fastest.
+ * runs of 16 KiB (32 or more ranks, long shards) or 1 KiB (otherwise); a row
+ * that starts mid-line touches one more line per run (at N = 128 on the
+ * GPT-175B block: 0.45% more HBM reads and a 1% slower reduction than
+ * line-aligned rows; 6.25% and 6% with 1 KiB runs).  Any layout works; this
+ * one is fastest.
  * Host only.  Errors: FSDP_E_ARG (null unit or pitch). */
 FSDP_API fsdp_status fsdp_unit_recv_pitch(const fsdp_unit* unit, int64_t* pitch);
 
