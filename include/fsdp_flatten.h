@@ -24,8 +24,10 @@
  *     (a hipStream_t; NULL is the default stream) and return.  Buffers must
  *     stay alive until that work has finished.
  *   - Errors: every argument is validated on the host, before any HIP call;
- *     a call that returns non-FSDP_OK has launched nothing and written
- *     nothing.  FSDP_E_HIP means a launch failed (hipGetLastError).  Faults
+ *     a call that returns any status but FSDP_OK or FSDP_E_HIP has launched
+ *     nothing and written nothing.  FSDP_E_HIP means a launch failed
+ *     (hipGetLastError); a call that launches several kernels may have
+ *     enqueued the ones before it.  Faults
  *     inside kernels surface at the caller's next synchronisation, as for any
  *     HIP work.  fsdp_last_error() returns a message for the calling thread's
  *     last non-OK status.
@@ -33,8 +35,10 @@
  *     with 16-byte loads where it sits (a scalar head first aligns outputs),
  *     and bf16 data at odd element offsets is realigned in the kernels.
  *     Misaligned below the element size is FSDP_E_ALIGN.
- *   - No call allocates, synchronises or records a memset, so every call can
- *     be captured in a HIP graph and replayed.
+ *   - No call allocates device memory, synchronises or records a memset, so
+ *     every call can be captured in a HIP graph and replayed.  Calls build
+ *     small host tables; if host memory runs out they return FSDP_E_NOMEM.
+ *     No C++ exception leaves the library.
  *   - Inputs and outputs must not overlap, except that fsdp_adam_shard updates
  *     param, exp_avg and exp_avg_sq in place.
  *   - A unit with no elements makes every call a no-op that returns FSDP_OK.
@@ -65,7 +69,7 @@ typedef enum {
     FSDP_E_RANGE = 2,        /* value out of its range (N, k, beta, step ...) */
     FSDP_E_ALIGN = 3,        /* pointer not aligned to its element size       */
     FSDP_E_OVERFLOW = 4,     /* a size overflows int64                        */
-    FSDP_E_NOMEM = 5,        /* host allocation of the unit plan failed       */
+    FSDP_E_NOMEM = 5,        /* host memory exhausted (plan or launch tables) */
     FSDP_E_HIP = 6,          /* a HIP runtime call or kernel launch failed    */
     FSDP_E_UNSUPPORTED = 7   /* valid request the library does not handle     */
 } fsdp_status;
