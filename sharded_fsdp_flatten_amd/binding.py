@@ -132,7 +132,8 @@ def _is_tensor(x) -> bool:
 
 
 def _addr(x, want=None) -> int:
-    """Device address of a tensor (checked contiguous and of dtype `want`), or an int."""
+    """Device address of a tensor (checked on the GPU, contiguous and of dtype `want`), or an
+    int taken as a device address."""
     if x is None:
         return 0
     if isinstance(x, int):
@@ -140,6 +141,10 @@ def _addr(x, want=None) -> int:
     if _is_tensor(x):
         if want is not None and str(x.dtype) not in want:
             raise TypeError("expected a tensor of dtype %s, got %s" % (" or ".join(want), x.dtype))
+        if not getattr(x, "is_cuda", False):
+            # a host address would reach the kernels and fault the GPU
+            raise ValueError("tensors passed to the library must be on the GPU, got one on %s"
+                             % x.device)
         if not x.is_contiguous():
             raise ValueError("tensors passed to the library must be contiguous")
         return int(x.data_ptr())

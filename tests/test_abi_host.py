@@ -445,3 +445,21 @@ def test_unscale_and_sqnorm_errors(B):
     assert lib.fsdp_grad_unscale(e.handle, 0, None, 0.5, None, None) == 0
     assert lib.fsdp_grad_sqnorm_workspace(e.handle, 0, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.fsdp_grad_sqnorm(e.handle, 0, None, None, 0, None, None) == 0
+
+
+def test_binding_refuses_host_tensors(B):
+    """A host tensor's address would reach the kernels and fault the GPU: the binding refuses
+    it before the library is called (and refuses non-contiguous tensors and wrong dtypes)."""
+    import torch
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(5, 3), (7,)], 2)
+    params = [torch.zeros(5, 3), torch.zeros(7)]
+    with pytest.raises(ValueError, match="on the GPU"):
+        B.fsdp_flatten_shard(u, params, 0, FAKE, stream=0)
+    with pytest.raises(ValueError, match="on the GPU"):
+        B.fsdp_flatten_shard(u, [FAKE, FAKE], 0, torch.zeros(u.S), stream=0)
+    with pytest.raises(ValueError, match="on the GPU"):
+        B.fsdp_grad_reduce_shard(u, [torch.zeros(u.S, dtype=torch.bfloat16)] * 2, 1.0, 1.0, FAKE,
+                                 stream=0)
+    with pytest.raises(TypeError, match="dtype"):
+        B.fsdp_adam_shard(u, torch.zeros(u.S, dtype=torch.float64), FAKE, FAKE, FAKE, lr=1e-3,
+                          stream=0)
