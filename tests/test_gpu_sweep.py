@@ -132,3 +132,64 @@ def test_sweep_special_values(pre, post):
     assert_f32_tol_then_bits(got, want, "sweep specials pre=%g post=%g" % (pre, post))
     for lo in zero_cols:
         assert np.all(got[lo:lo + 9].view(np.uint32) == 0x80000000), "-0 column at %d" % lo
+
+
+_FRESH_CAPTURE = r"""
+import sys
+sys.path.insert(0, %(root)r)
+import numpy as np, torch
+import workloads as W
+from sharded_fsdp_flatten_amd import binding as B
+N, S = 32, %(S)d
+u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+c = W.device_contribs(N, S, step=7, pitch=-(-S // 64) * 64)
+rows = [c[r] for r in range(N)]
+out_g = torch.empty(S, device="cuda:0")
+out_e = torch.empty(S, device="cuda:0")
+torch.cuda.synchronize()
+g = torch.cuda.CUDAGraph()
+with torch.cuda.graph(g):  # the library's first call in this process is captured
+    B.fsdp_grad_reduce_shard(u, rows, 4.0, 8.0, out_g)
+B.fsdp_grad_reduce_shard(u, rows, 4.0, 8.0, out_e)
+for rep in range(3):
+    out_g.fill_(float("nan"))
+    g.replay()
+    torch.cuda.synchronize()
+    assert torch.equal(out_g.view(torch.int32), out_e.view(torch.int32)), rep
+print("fresh-capture OK", flush=True)
+"""
+
+
+def test_sweep_first_call_captured_in_a_fresh_process():
+    """The sweep reads the device's occupancy on its first call; that call may be the one a
+    caller captures into a HIP graph.  A child process whose first library call is captured,
+    replayed three times and compared bit for bit with an eager call.  (Had the runtime refused
+    the query during capture, the captured call would have taken the tile kernel: the result
+    must be the same bits either way, and the capture must not fail.)"""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = _FRESH_CAPTURE % {"root": root, "S": MIN_TILES * TILE + 5}
+    p = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, timeout=150)
+    assert p.returncode == 0 and "fresh-capture OK" in p.stdout, p.stdout[-2000:] + p.stderr[-3000:]
+
+
+def test_sweep_result_does_not_depend_on_residency():
+    """The sweep's grid is sized to be resident at once, but no wave waits for another: with a
+    long kernel holding CUs on a second stream, the result is bit-identical."""
+    N, S = 32, MIN_TILES * TILE + 100
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    c, ch = _contribs(N, S, step=8)
+    alone = _reduce(u, c, 2.0, 16.0)
+    side = torch.cuda.Stream()
+    big = torch.randn(1 << 28, device=dev())
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(4):
+            big.mul_(1.0001).add_(1e-7)  # keeps CUs busy while the reduction runs
+    shared = _reduce(u, c, 2.0, 16.0)
+    torch.cuda.synchronize()
+    assert torch.equal(alone.view(torch.int32), shared.view(torch.int32))
+    assert_f32_tol_then_bits(to_host(shared), oracle.grad_reduce(list(ch), 2.0, 16.0),
+                             "sweep beside another stream")
