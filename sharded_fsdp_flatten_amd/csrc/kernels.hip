@@ -8,7 +8,9 @@
 //   - ONE SMALL TILE PER WORKGROUP (1-2 KiB per wave), never a persistent
 //     grid-stride loop: the dispatcher then keeps the workgroups in flight on a
 //     compact address window, which HBM serves with far fewer row switches
-//     (a grid-stride version of the same copy runs ~20% slower);
+//     (a grid-stride version of the same copy runs ~20% slower).  The one
+//     exception is the many-rank reduction's sweep (below): there the window
+//     that matters is over ranks, and a longer run per wave keeps it compact;
 //   - outputs stored non-temporally (streamed, never re-read by the kernel).
 // The kernels:
 //   - segcopy: one engine for flatten (FSDP1 and FSDP2), copy-out, the cast and
