@@ -116,3 +116,30 @@ def test_adamw_on_a_shard_beyond_2_31_elements():
     assert_f32_tol_then_bits(to_host(v.index_select(0, ti)), hv, "adamw v samples")
     assert_bf16_bits(to_host(pb.view(torch.int16).index_select(0, ti)).view(np.uint16), hpb,
                      "adamw bf16 samples")
+
+
+def test_many_rank_sweep_over_a_shard_beyond_2_31_elements():
+    """32 ranks of 2^31 + 1000 outputs (137 GB of contributions): the row-major sweep, split
+    into ~130 runs of resident waves, with tile offsets past 2^31 and a cut tile at the end.
+    Contributions follow a position-dependent pattern of small integers times 2^-10 (exact in
+    bf16; a misread column shows); outputs are checked against the oracle on samples."""
+    N, S = 32, BIG + 1000
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    assert u.S == S
+    c = torch.empty((N, S), dtype=torch.bfloat16, device=dev())
+    idx = torch.arange(S, dtype=torch.int64, device=dev())
+    for r in range(N):
+        t = idx.mul(2 * r + 1)
+        t.add_(7 * r).remainder_(251).sub_(125)
+        c[r].copy_(t.to(torch.float32).mul_(2.0 ** -10))
+        del t
+    del idx
+    torch.cuda.empty_cache()
+    out = torch.empty(S, device=dev())
+    B.fsdp_grad_reduce_shard(u, [c[r] for r in range(N)], 4.0, 8.0, out)
+    _sync()
+    sample = _sample_idx(S, 9)
+    ti = torch.from_numpy(sample).to(dev())
+    cs = [to_host(c[r].view(torch.int16).index_select(0, ti)).view(np.uint16) for r in range(N)]
+    assert_f32_tol_then_bits(to_host(out.index_select(0, ti)), oracle.grad_reduce(cs, 4.0, 8.0),
+                             "sweep samples beyond 2^31")
