@@ -463,3 +463,40 @@ def test_binding_refuses_host_tensors(B):
     with pytest.raises(TypeError, match="dtype"):
         B.fsdp_adam_shard(u, torch.zeros(u.S, dtype=torch.float64), FAKE, FAKE, FAKE, lr=1e-3,
                           stream=0)
+
+
+def test_last_error_is_per_thread(B):
+    """fsdp_last_error() holds the calling thread's message: 8 threads fail calls with
+    different messages at the same time (ctypes releases the GIL around foreign calls) and each
+    must read back its own, then a successful call must leave its thread's message empty."""
+    import ctypes
+    import threading
+    lib = B.load()
+    errors = []
+
+    def work(tid):
+        try:
+            u = B.fsdp_unit_create(B.FSDP_FLAT, [(4 + tid,)], 2)
+            for it in range(300):
+                if (it + tid) % 2:
+                    st = lib.fsdp_unit_create(1, 1, None, None, 2, None)  # out NULL
+                    want = b"out is NULL"
+                else:
+                    st = lib.fsdp_unit_param_offset(u.handle, 5 + tid, None)  # offset NULL
+                    want = b"must not be NULL"
+                msg = lib.fsdp_last_error()
+                if st == 0 or want not in msg:
+                    errors.append((tid, it, st, msg))
+                    return
+            sizes = B.fsdp_unit_sizes()
+            if lib.fsdp_unit_info(u.handle, -1, ctypes.byref(sizes)) != 0 or lib.fsdp_last_error() != b"":
+                errors.append((tid, "ok call left a message"))
+        except Exception as e:  # noqa: BLE001 - reported below
+            errors.append((tid, repr(e)))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
