@@ -193,3 +193,53 @@ def test_sweep_result_does_not_depend_on_residency():
     assert torch.equal(alone.view(torch.int32), shared.view(torch.int32))
     assert_f32_tol_then_bits(to_host(shared), oracle.grad_reduce(list(ch), 2.0, 16.0),
                              "sweep beside another stream")
+
+
+_FRESH_THREADS = r"""
+import sys, threading
+sys.path.insert(0, %(root)r)
+import torch
+import workloads as W
+from sharded_fsdp_flatten_amd import binding as B
+S = %(S)d
+jobs = [(32, 1), (48, 2), (8, 3), (64, 4)]  # (ranks, step): sweeps and one tile-kernel case
+units, rows, outs = [], [], []
+for N, step in jobs:
+    units.append(B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N))
+    c = W.device_contribs(N, S, step=step, pitch=-(-S // 64) * 64)
+    rows.append([c[r] for r in range(N)])
+    outs.append(torch.empty(S, device="cuda:0"))
+torch.cuda.synchronize()
+errors = []
+def work(i):
+    try:
+        s = torch.cuda.Stream()
+        with torch.cuda.stream(s):
+            B.fsdp_grad_reduce_shard(units[i], rows[i], 2.0, 8.0, outs[i], stream=s)
+        s.synchronize()
+    except Exception as e:
+        errors.append(repr(e))
+ts = [threading.Thread(target=work, args=(i,)) for i in range(len(jobs))]
+for t in ts: t.start()
+for t in ts: t.join()
+assert not errors, errors
+for i in range(len(jobs)):
+    ref = torch.empty(S, device="cuda:0")
+    B.fsdp_grad_reduce_shard(units[i], rows[i], 2.0, 8.0, ref)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.view(torch.int32), outs[i].view(torch.int32)), i
+print("threads OK", flush=True)
+"""
+
+
+def test_concurrent_first_calls_from_threads_in_a_fresh_process():
+    """Four host threads make their first library calls at the same time, each on its own
+    stream (three sweeps and one tile-kernel reduction): the per-device occupancy value is
+    initialised concurrently, and every result equals a later single-threaded call."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    script = _FRESH_THREADS % {"root": root, "S": MIN_TILES * TILE + 3}
+    p = subprocess.run([sys.executable, "-c", script], capture_output=True, text=True, timeout=200)
+    assert p.returncode == 0 and "threads OK" in p.stdout, p.stdout[-2000:] + p.stderr[-3000:]
