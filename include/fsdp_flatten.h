@@ -193,6 +193,10 @@ FSDP_API fsdp_status fsdp_unit_recv_pitch(const fsdp_unit* unit, int64_t* pitch)
  * FLAT writes shard[j] = F[k*S + j] with F the padded flat buffer; ROWS writes
  * rank k's segment (its rows of every parameter, zero rows up to c_i).
  * Results are bit-exact copies.
+ * Errors: FSDP_E_ARG (NULL unit; NULL params table or entry of a non-empty
+ * parameter; NULL shard with elements to write), FSDP_E_RANGE (k neither in
+ * [0, N) nor FSDP_ALL_RANKS), FSDP_E_ALIGN (a pointer not 4-byte aligned),
+ * FSDP_E_NOMEM, FSDP_E_HIP.
  */
 FSDP_API fsdp_status fsdp_flatten_shard(const fsdp_unit* unit, const float* const* params, int32_t k,
                                float* shard, void* stream);
@@ -208,6 +212,9 @@ FSDP_API fsdp_status fsdp_flatten_shard(const fsdp_unit* unit, const float* cons
  *              FLAT padding is never read.
  *   outs     : host array of n_params device pointers, output i holding numel_i
  *              bf16 elements (NULL allowed for zero-size parameters).
+ * Errors: FSDP_E_ARG (NULL unit; NULL gathered with T > 0; NULL outs table or
+ * entry of a non-empty parameter), FSDP_E_ALIGN (gathered not 4-byte or an
+ * output not 2-byte aligned), FSDP_E_NOMEM, FSDP_E_HIP.
  */
 FSDP_API fsdp_status fsdp_unflatten_copyout(const fsdp_unit* unit, const float* gathered,
                                    uint16_t* const* outs, void* stream);
@@ -225,6 +232,10 @@ FSDP_API fsdp_status fsdp_unflatten_copyout(const fsdp_unit* unit, const float* 
  *   grad_shard  : device pointer, S fp32 outputs.
  * out[j] = ((c_0[j]/pre + c_1[j]/pre) + ... + c_{N-1}[j]/pre) / post, each
  * operation one rounded binary32 operation, summed in rank order from rank 0.
+ * Errors: FSDP_E_ARG (NULL unit; with S > 0, a NULL contribs table or entry, or
+ * a NULL grad_shard), FSDP_E_RANGE (pre_divide or post_divide zero or not
+ * finite), FSDP_E_ALIGN (a contribution not 2-byte or grad_shard not 4-byte
+ * aligned), FSDP_E_NOMEM, FSDP_E_HIP.
  */
 FSDP_API fsdp_status fsdp_grad_reduce_shard(const fsdp_unit* unit, const uint16_t* const* contribs,
                                    float pre_divide, float post_divide, float* grad_shard,
@@ -243,6 +254,11 @@ FSDP_API fsdp_status fsdp_grad_reduce_shard(const fsdp_unit* unit, const uint16_
  * step_size = lr/(1 - beta1^t), bc2s = sqrt(1 - beta2^t).  Per element, each
  * a rounded binary32 operation: p = p*decay; m = beta1*m + (1-beta1)*g;
  * v = beta2*v + (1-beta2)*(g*g); p = p - step_size*(m/(sqrt(v)/bc2s + eps)).
+ * Errors: FSDP_E_ARG (NULL unit or cfg; with S > 0, a NULL param, grad,
+ * exp_avg or exp_avg_sq), FSDP_E_RANGE (step < 1; beta1 or beta2 outside
+ * [0, 1); lr or weight_decay not finite; eps negative or not finite),
+ * FSDP_E_ALIGN (an fp32 pointer not 4-byte or param_bf16 not 2-byte aligned),
+ * FSDP_E_NOMEM, FSDP_E_HIP.
  */
 FSDP_API fsdp_status fsdp_adam_shard(const fsdp_unit* unit, float* param, const float* grad,
                             float* exp_avg, float* exp_avg_sq, const fsdp_adamw_cfg* cfg,
@@ -262,6 +278,8 @@ FSDP_API fsdp_status fsdp_adam_shard(const fsdp_unit* unit, float* param, const 
  * [P2] section 5: FSDP2 gathers the bf16 copy); the same cast turns an
  * fp32-accumulated gradient into the bf16 ReduceScatter input.
  *   src : device pointer, fp32.   dst : device pointer, bf16 (same count).
+ * Errors: FSDP_E_ARG (NULL unit; NULL src or dst with elements to cast),
+ * FSDP_E_RANGE (k), FSDP_E_ALIGN, FSDP_E_NOMEM, FSDP_E_HIP.
  */
 FSDP_API fsdp_status fsdp_cast_to_bf16(const fsdp_unit* unit, int32_t k, const float* src,
                                        uint16_t* dst, void* stream);
@@ -273,6 +291,7 @@ FSDP_API fsdp_status fsdp_cast_to_bf16(const fsdp_unit* unit, int32_t k, const f
  * gather.  Bit-identical to casting after the gather.
  *   gathered : device pointer, bf16.   outs : host array of n_params device
  *   pointers, bf16, numel_i each (NULL allowed for zero-size parameters).
+ * Errors as fsdp_unflatten_copyout (gathered 2-byte aligned).
  */
 FSDP_API fsdp_status fsdp_unflatten_copyout_bf16(const fsdp_unit* unit, const uint16_t* gathered,
                                                  uint16_t* const* outs, void* stream);
@@ -286,6 +305,7 @@ FSDP_API fsdp_status fsdp_unflatten_copyout_bf16(const fsdp_unit* unit, const ui
  * the unsharded gradient in the FlatParameter layout for FSDP1).
  *   params : host array of n_params device pointers, bf16.
  *   shard  : device pointer, bf16, S elements (L for FSDP_ALL_RANKS).
+ * Errors as fsdp_flatten_shard (pointers 2-byte aligned).
  */
 FSDP_API fsdp_status fsdp_flatten_shard_bf16(const fsdp_unit* unit, const uint16_t* const* params,
                                              int32_t k, uint16_t* shard, void* stream);
@@ -315,6 +335,8 @@ FSDP_API fsdp_status fsdp_grad_reduce_shard_ex(const fsdp_unit* unit, const uint
  * acc[j] = (init ? 0 : acc[j]) + fp32(grad[j]) over rank k's shard (S elements)
  * or, with k == FSDP_ALL_RANKS, the whole unsharded layout (L elements).
  *   grad : device pointer, bf16.   acc : device pointer, fp32, updated in place.
+ * Errors: FSDP_E_ARG (NULL unit; NULL grad or acc with elements to add),
+ * FSDP_E_RANGE (k), FSDP_E_ALIGN, FSDP_E_NOMEM, FSDP_E_HIP.
  */
 FSDP_API fsdp_status fsdp_grad_accumulate(const fsdp_unit* unit, int32_t k, const uint16_t* grad,
                                           float* acc, int32_t init, void* stream);

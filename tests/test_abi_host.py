@@ -500,3 +500,88 @@ def test_last_error_is_per_thread(B):
     for t in threads:
         t.join()
     assert not errors, errors[:3]
+
+
+def test_documented_error_statuses(B):
+    """Every per-call 'Errors:' line of include/fsdp_flatten.h, condition by condition, returns
+    the status it names (addresses are never dereferenced: validation precedes any HIP call)."""
+    import ctypes
+    lib = B.load()
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(6, 5), (7,)], 4)
+    h = u.handle
+    tab2 = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    tab2_null = (ctypes.c_void_p * 2)(FAKE, None)
+    tab2_odd = (ctypes.c_void_p * 2)(FAKE, FAKE + 1)
+    tab2_two = (ctypes.c_void_p * 2)(FAKE, FAKE + 2)
+    tab4 = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE, FAKE)
+    tab4_null = (ctypes.c_void_p * 4)(FAKE, FAKE, None, FAKE)
+    tab4_odd = (ctypes.c_void_p * 4)(FAKE, FAKE, FAKE + 1, FAKE)
+    c = lambda t: ctypes.cast(t, ctypes.c_void_p)  # noqa: E731
+
+    def adam(**kw):
+        cfg = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0, step=1)
+        ptrs = kw.pop("ptrs", (FAKE, FAKE, FAKE, FAKE))
+        pb = kw.pop("pb", None)
+        cfg.update(kw)
+        s = B.fsdp_adamw_cfg(cfg["lr"], cfg["beta1"], cfg["beta2"], cfg["eps"], cfg["weight_decay"],
+                             cfg["step"])
+        return lib.fsdp_adam_shard(h, *ptrs, ctypes.byref(s), pb, None)
+
+    inf, nan = float("inf"), float("nan")
+    cases = [
+        # flatten
+        (lambda: lib.fsdp_flatten_shard(None, c(tab2), 0, FAKE, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_flatten_shard(h, None, 0, FAKE, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_flatten_shard(h, c(tab2_null), 0, FAKE, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_flatten_shard(h, c(tab2), 0, None, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_flatten_shard(h, c(tab2), 4, FAKE, None), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_flatten_shard(h, c(tab2), -2, FAKE, None), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_flatten_shard(h, c(tab2_two), 0, FAKE, None), "FSDP_E_ALIGN"),
+        (lambda: lib.fsdp_flatten_shard(h, c(tab2), 0, FAKE + 2, None), "FSDP_E_ALIGN"),
+        # copy-out
+        (lambda: lib.fsdp_unflatten_copyout(None, FAKE, c(tab2), None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unflatten_copyout(h, None, c(tab2), None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unflatten_copyout(h, FAKE, None, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unflatten_copyout(h, FAKE, c(tab2_null), None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unflatten_copyout(h, FAKE + 2, c(tab2), None), "FSDP_E_ALIGN"),
+        (lambda: lib.fsdp_unflatten_copyout(h, FAKE, c(tab2_odd), None), "FSDP_E_ALIGN"),
+        # reduce
+        (lambda: lib.fsdp_grad_reduce_shard(None, c(tab4), 1.0, 1.0, FAKE, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_grad_reduce_shard(h, None, 1.0, 1.0, FAKE, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_grad_reduce_shard(h, c(tab4_null), 1.0, 1.0, FAKE, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_grad_reduce_shard(h, c(tab4), 1.0, 1.0, None, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_grad_reduce_shard(h, c(tab4), 0.0, 1.0, FAKE, None), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_grad_reduce_shard(h, c(tab4), 1.0, inf, FAKE, None), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_grad_reduce_shard(h, c(tab4), nan, 1.0, FAKE, None), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_grad_reduce_shard(h, c(tab4_odd), 1.0, 1.0, FAKE, None), "FSDP_E_ALIGN"),
+        (lambda: lib.fsdp_grad_reduce_shard(h, c(tab4), 1.0, 1.0, FAKE + 2, None), "FSDP_E_ALIGN"),
+        # AdamW
+        (lambda: lib.fsdp_adam_shard(None, FAKE, FAKE, FAKE, FAKE, None, None, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_adam_shard(h, FAKE, FAKE, FAKE, FAKE, None, None, None), "FSDP_E_ARG"),
+        (lambda: adam(ptrs=(FAKE, FAKE, None, FAKE)), "FSDP_E_ARG"),
+        (lambda: adam(step=0), "FSDP_E_RANGE"),
+        (lambda: adam(beta1=1.0), "FSDP_E_RANGE"),
+        (lambda: adam(beta2=-0.1), "FSDP_E_RANGE"),
+        (lambda: adam(lr=nan), "FSDP_E_RANGE"),
+        (lambda: adam(weight_decay=inf), "FSDP_E_RANGE"),
+        (lambda: adam(eps=-1e-8), "FSDP_E_RANGE"),
+        (lambda: adam(eps=inf), "FSDP_E_RANGE"),
+        (lambda: adam(ptrs=(FAKE, FAKE + 2, FAKE, FAKE)), "FSDP_E_ALIGN"),
+        (lambda: adam(pb=FAKE + 1), "FSDP_E_ALIGN"),
+        # cast, bf16 copy-out, bf16 flatten, local accumulation
+        (lambda: lib.fsdp_cast_to_bf16(None, 0, FAKE, FAKE, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_cast_to_bf16(h, 0, None, FAKE, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_cast_to_bf16(h, 4, FAKE, FAKE, None), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_cast_to_bf16(h, 0, FAKE, FAKE + 1, None), "FSDP_E_ALIGN"),
+        (lambda: lib.fsdp_unflatten_copyout_bf16(h, FAKE + 1, c(tab2), None), "FSDP_E_ALIGN"),
+        (lambda: lib.fsdp_unflatten_copyout_bf16(h, None, c(tab2), None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_flatten_shard_bf16(h, c(tab2_odd), 0, FAKE, None), "FSDP_E_ALIGN"),
+        (lambda: lib.fsdp_flatten_shard_bf16(h, c(tab2), 9, FAKE, None), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_grad_accumulate(None, 0, FAKE, FAKE, 1, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_grad_accumulate(h, 0, FAKE, None, 1, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_grad_accumulate(h, -3, FAKE, FAKE, 1, None), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_grad_accumulate(h, 0, FAKE + 1, FAKE, 1, None), "FSDP_E_ALIGN"),
+    ]
+    for i, (call, want) in enumerate(cases):
+        got = B.STATUS_NAMES.get(call(), "?")
+        assert got == want, (i, got, want, lib.fsdp_last_error())
