@@ -81,6 +81,11 @@ def parse_args():
     ap.add_argument("--copy-probe", action="store_true",
                     help="also time a plain 4 GiB fp32 copy through the library (N = 1 unit) "
                          "and hipMemcpy device-to-device, as copy ceilings")
+    ap.add_argument("--floor-probe", action="store_true",
+                    help="also run the library's fp32 copy (flatten of a one-parameter unit, N = 1) "
+                         "at 8 MB .. 1 GB of traffic, 20 launches per size, each after a 1 GiB "
+                         "read: the fixed cost and rate of a cold-cache copy, for rocprofv3's "
+                         "kernel trace (the event times reported here include event overhead)")
     return ap.parse_args()
 
 
@@ -514,6 +519,29 @@ def main():
                            "GB/s": round(8 * n / (ms * 1e-3) / 1e9, 1)}
         result["copy_ceiling"] = probe
         del a, b
+
+    if args.floor_probe:
+        fb = torch.zeros(1 << 28, device=dev)
+        fs = torch.zeros((), device=dev)
+        a = torch.randn(1 << 27, device=dev, generator=gen)
+        b = torch.empty(1 << 27, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        floor = []
+        for lg in range(20, 28):
+            n = 1 << lg
+            cu = B.fsdp_unit_create(B.FSDP_FLAT, [(n,)], 1)
+            ts = []
+            for _ in range(20):
+                torch.sum(fb, dim=0, out=fs)  # evicts the source and destination
+                e0.record(stream)
+                B.fsdp_flatten_shard(cu, [a[:n]], 0, b[:n])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            ts.sort()
+            floor.append({"elements": n, "bytes": 8 * n, "event_ms_median": round(ts[len(ts) // 2], 4)})
+        result["floor_probe"] = floor
+        del a, b, fb
 
     if not args.no_cpu_baseline:
         host = {
