@@ -69,10 +69,12 @@ def parse_args():
                          "the 256 MB Infinity Cache (auto: on when the copy-out moves < 2 GB, where "
                          "the step order alone does not guarantee it); with flushing, the step time "
                          "is the sum of the kernels' event times")
-    ap.add_argument("--sweep-ranks", action="store_true",
-                    help="also time flatten, reduce and AdamW for every rank (N <= 8) or for ranks "
-                         "0, 1, N/2-1, N-1, each launch after a 1 GiB read flush; reports the worst "
-                         "rank")
+    ap.add_argument("--sweep-ranks", dest="sweep_ranks", action="store_true", default=True,
+                    help="(default) also time flatten, reduce and AdamW for every rank (N <= 8) or "
+                         "for ranks 0, 1, N/2-1, N-1, each launch after a 1 GiB read flush, and "
+                         "report the worst rank beside the headline rank (`per_rank`)")
+    ap.add_argument("--no-sweep-ranks", dest="sweep_ranks", action="store_false",
+                    help="skip the rank sweep")
     ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
                     help="replay the step from a captured HIP graph (the four launches recorded once, "
                          "no host launch overhead per step).  auto: on when no flush is needed, and "
