@@ -262,7 +262,10 @@ def sweep_ranks(B, u, N, contrib_rows, pre, post, hp, params, grad, shard, adam_
     flatten reads only rank k's real elements."""
     import torch
     ks = list(range(N)) if N <= 8 else sorted({0, 1, max(0, N // 2 - 1), N - 1})
-    out = {"ranks": ks, "reps": reps}
+    out = {"ranks": ks, "reps": reps,
+           "timing": "one HIP event pair around each single launch, each after a 1 GiB read; the "
+                     "pair adds 2-5 us per launch, a few percent on kernels of 20-60 us (kernel "
+                     "durations without it: rocprofv3, profiles/)"}
     worst = {}
     for k in ks:
         info = u.info(k)
