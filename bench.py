@@ -448,6 +448,9 @@ def main():
                    "step_time": ("sum of the kernels' event times, 1 GiB read before each kernel"
                                  if flush_on else "wall clock")},
         "kernels": kernels,
+        "kernel_timing": ("HIP events recorded around each launch on its stream in the eager loop; "
+                          "an event pair adds 2-5 us, a few percent on the short kernels (flatten, "
+                          "AdamW); rocprofv3 kernel durations are in profiles/"),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
