@@ -68,3 +68,24 @@ def test_bench_headline_from_graph_replays_without_flush():
     step_bytes = sum(k["bytes"] for k in d["kernels"].values())
     assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"] + 0.1
     assert d["eager"]["ms_per_step"] > 0 and "graph" not in d
+
+
+def test_bench_defaults_probes_and_opt_outs():
+    """The rank sweep is on by default (and --no-sweep-ranks removes it); the copy and floor
+    probes report what they measure; every line says how its kernel times were taken."""
+    p = _run("--workload", "tiny", "--steps", "2", "--warmup", "1", "--no-cpu-baseline",
+             "--no-next", "--copy-probe", "--floor-probe")
+    assert p.returncode == 0, p.stderr[-2000:]
+    d = json.loads([l for l in p.stdout.splitlines() if l.startswith("{")][0])
+    assert "per_rank" in d and "timing" in d["per_rank"] and "kernel_timing" in d
+    assert "next_rows" not in d
+    cp = d["copy_ceiling"]
+    assert set(cp) == {"library_copy", "hipMemcpyDtoD"} and all(v["GB/s"] > 0 for v in cp.values())
+    fl = d["floor_probe"]
+    assert [f["elements"] for f in fl] == [1 << lg for lg in range(20, 28)]
+    assert all(f["bytes"] == 8 * f["elements"] and f["event_ms_median"] > 0 for f in fl)
+    p = _run("--workload", "tiny", "--steps", "2", "--warmup", "1", "--no-cpu-baseline",
+             "--no-next", "--no-sweep-ranks")
+    assert p.returncode == 0, p.stderr[-2000:]
+    d = json.loads([l for l in p.stdout.splitlines() if l.startswith("{")][0])
+    assert "per_rank" not in d
