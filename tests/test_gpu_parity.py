@@ -93,6 +93,45 @@ def test_flat_flatten_every_rank(name, N):
         assert_f32_bits(to_host(outs[k]), oracle.flat_shard(params, N, k), "%s N=%d k=%d" % (name, N, k))
 
 
+def test_flat_parameter_order_moves_only_the_straddles():
+    """Reading c of the unit order: the caller's list order.  The GPT-2-L block in module
+    registration order (ln1, attention, ln2, MLP) instead of the config order: every rank's
+    shard and the gathered layout against the oracle bit for bit, the same sizes, the same
+    multiset of flat values, and every parameter's bf16 copy-out identical in both orders."""
+    unit = W.gpt2_large_block(N=8)
+    reg = [0, 1, 4, 5, 6, 7, 2, 3, 8, 9, 10, 11]  # ln1.w/b, qkv, proj, ln2.w/b, fc, fc2
+    assert [unit.names[i] for i in reg][:6] == ["ln1.w", "ln1.b", "attn.qkv.w", "attn.qkv.b",
+                                                "attn.proj.w", "attn.proj.b"]
+    params = W.host_params(unit, seed=0)
+    for N in (8, 7):
+        orders = {}
+        for name, idx in (("config", list(range(12))), ("registration", reg)):
+            shapes = [unit.shapes[i] for i in idx]
+            ps = [params[i] for i in idx]
+            u = B.fsdp_unit_create(B.FSDP_FLAT, shapes, N)
+            d_ps = [to_dev(q) for q in ps]
+            gathered = torch.full((u.L,), float("nan"), device=dev())
+            B.fsdp_flatten_shard(u, d_ps, B.FSDP_ALL_RANKS, gathered)
+            shard = torch.empty(u.S, device=dev())
+            for k in range(N):
+                B.fsdp_flatten_shard(u, d_ps, k, shard)
+                _sync()
+                assert_f32_bits(to_host(shard), oracle.flat_shard(ps, N, k),
+                                "%s order N=%d k=%d" % (name, N, k))
+            outs = [torch.empty(sh, dtype=torch.bfloat16, device=dev()) for sh in shapes]
+            B.fsdp_unflatten_copyout(u, gathered, outs)
+            _sync()
+            g = to_host(gathered)
+            assert_f32_bits(g, oracle.flat_shard(ps, N, -1), "%s order N=%d gathered" % (name, N))
+            by_param = {idx[j]: to_host(outs[j]) for j in range(12)}
+            orders[name] = (u.S, u.L, np.sort(g.view(np.uint32)), by_param)
+        a, b = orders["config"], orders["registration"]
+        assert a[0] == b[0] and a[1] == b[1]
+        assert np.array_equal(a[2], b[2])
+        for i in range(12):
+            assert np.array_equal(a[3][i], b[3][i]), unit.names[i]
+
+
 def test_flat_flatten_fig3_units():
     for shapes in ([(3, 4), (3,)], [(4, 3), (4,)]):
         params = [np.arange(np.prod(s), dtype=np.float32).reshape(s) + 1 for s in shapes]
