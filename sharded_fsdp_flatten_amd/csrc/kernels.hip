@@ -1074,31 +1074,25 @@ int64_t sweep_capacity() {
     return c > 0 ? c : 0;
 }
 
-// The sweep over this launch's ranks: the whole tiles are split into as few runs as
-// keep every run's grid (cut tile, fewer than kSweepV single tiles, the waves)
-// resident at once, one launch per run in output order; *err gets the first launch
-// error.  Returns false, having launched nothing, when the output is too short or the
-// occupancy is unknown.
+// The sweep over this launch's ranks, one launch per run of plan_sweep_runs (runs whose
+// grids are resident at once), in output order; *err gets the first launch error.  Returns
+// false, having launched nothing, when the output is too short or the occupancy unknown.
 template <int kPre, bool kAccum>
 bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
     constexpr int64_t kTile = 512;
     const int64_t tiles = a.len / kTile;
-    if (tiles < kSweepV || tiles < FSDP_SWEEP_MIN_TILES) return false;
-    const int64_t cap = sweep_capacity<kPre, kAccum>();
-    if (cap <= kSweepV + 1) return false;
-    const int64_t per_run = kSweepV * (cap - kSweepV);  // blocks <= per_run / kV + kV - 1 + 1
-    const int64_t runs = (tiles + per_run - 1) / per_run;
-    const int64_t each = (tiles + runs - 1) / runs;
-    for (int64_t t = 0; t < tiles; t += each) {
-        const int64_t n = std::min(each, tiles - t);
+    if (tiles < FSDP_SWEEP_MIN_TILES) return false;
+    std::vector<SweepRun> runs;
+    if (!plan_sweep_runs(tiles, a.len % kTile != 0, kSweepV, sweep_capacity<kPre, kAccum>(), &runs))
+        return false;
+    for (const SweepRun& r : runs) {
         SweepArgs s{};
         s.r = a;
-        s.t_first = t;
-        s.cut = t + n == tiles && a.len % kTile != 0;
-        s.n_single = static_cast<int32_t>(n % kSweepV);
-        const int64_t blocks = s.cut + s.n_single + n / kSweepV;
+        s.t_first = r.t_first;
+        s.cut = r.cut;
+        s.n_single = r.n_single;
         hipLaunchKernelGGL((reduce_sweep_kernel<kPre, kAccum, kSweepV>),
-                           dim3(static_cast<unsigned>(blocks)), dim3(64), 0, stream, s);
+                           dim3(static_cast<unsigned>(r.blocks)), dim3(64), 0, stream, s);
         *err = hipGetLastError();
         if (*err != hipSuccess) break;
     }

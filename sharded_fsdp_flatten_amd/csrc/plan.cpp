@@ -328,4 +328,25 @@ void plan_param_runs(const UnitPlan& u, int64_t k, std::vector<ParamRun>* runs) 
     }
 }
 
+bool plan_sweep_runs(int64_t tiles, bool cut_tile, int64_t kv, int64_t capacity,
+                     std::vector<SweepRun>* runs) {
+    runs->clear();
+    if (kv < 1 || tiles < kv || capacity <= kv) return false;
+    // a run of n tiles takes cut + (n mod kv) + n/kv <= 1 + (kv - 1) + n/kv workgroups, so
+    // n <= kv * (capacity - kv) keeps it within capacity
+    const int64_t per_run = kv * (capacity - kv);
+    const int64_t n_runs = (tiles + per_run - 1) / per_run;
+    const int64_t each = (tiles + n_runs - 1) / n_runs;
+    for (int64_t t = 0; t < tiles; t += each) {
+        SweepRun r;
+        r.t_first = t;
+        r.n_tiles = std::min(each, tiles - t);
+        r.cut = (t + r.n_tiles == tiles && cut_tile) ? 1 : 0;
+        r.n_single = static_cast<int32_t>(r.n_tiles % kv);
+        r.blocks = r.cut + r.n_single + r.n_tiles / kv;
+        runs->push_back(r);
+    }
+    return true;
+}
+
 }  // namespace fsdp

@@ -79,4 +79,22 @@ struct ParamRun {
 };
 void plan_param_runs(const UnitPlan& u, int64_t k, std::vector<ParamRun>* runs);
 
+// One launch of the many-rank reduction's sweep: whole tiles [t_first, t_first + n_tiles)
+// of the output; its grid is `cut` workgroups for the tile the output's end cuts (only in
+// the last run), then n_single workgroups of one whole tile each (n_tiles mod kv), then one
+// workgroup per kv whole tiles: `blocks` workgroups in all.
+struct SweepRun {
+    int64_t t_first = 0;
+    int64_t n_tiles = 0;
+    int32_t cut = 0;
+    int32_t n_single = 0;
+    int64_t blocks = 0;
+};
+// Splits `tiles` whole tiles (plus a cut tile when `cut_tile`) into as few runs of nearly
+// equal length as keep every run's grid within `capacity` workgroups (those resident at
+// once), kv tiles per sweep workgroup.  Returns false, leaving `runs` empty, when tiles < kv
+// or capacity <= kv (no run fits).
+bool plan_sweep_runs(int64_t tiles, bool cut_tile, int64_t kv, int64_t capacity,
+                     std::vector<SweepRun>* runs);
+
 }  // namespace fsdp

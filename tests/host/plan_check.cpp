@@ -229,6 +229,39 @@ void check_overflow() {
     CHECK(fsdp::plan_create(fsdp::kFlat, 1, nd11, ok, 2147483647, &p, &err) == 0 && p.S == 1, "huge N");
 }
 
+// The reduction sweep's runs: for random tile counts, kv and capacities, the runs cover the
+// whole tiles [0, tiles) in order, each exactly once; every run's grid (cut + single tiles +
+// kv-tile workgroups) fits the capacity; only the last run has the cut tile; the split uses
+// the fewest runs the per-run bound allows.  Unusable inputs are refused.
+void check_sweep_runs(std::mt19937_64& rng, int iters) {
+    std::vector<fsdp::SweepRun> runs;
+    CHECK(!fsdp::plan_sweep_runs(15, true, 16, 2048, &runs) && runs.empty(), "tiles < kv refused");
+    CHECK(!fsdp::plan_sweep_runs(1000, false, 16, 16, &runs), "capacity <= kv refused");
+    CHECK(!fsdp::plan_sweep_runs(1000, false, 16, 0, &runs), "unknown capacity refused");
+    for (int it = 0; it < iters; ++it) {
+        const int64_t kv = 1 + static_cast<int64_t>(rng() % 20);
+        const int64_t cap = kv + 1 + static_cast<int64_t>(rng() % (it % 3 == 0 ? 40 : 5000));
+        const int64_t tiles = kv + static_cast<int64_t>(rng() % (it % 4 == 0 ? 200 : 20000000));
+        const bool cut = (rng() & 1) != 0;
+        CHECK(fsdp::plan_sweep_runs(tiles, cut, kv, cap, &runs) && !runs.empty(), "sweep planned");
+        const int64_t per_run = kv * (cap - kv);
+        CHECK(static_cast<int64_t>(runs.size()) == (tiles + per_run - 1) / per_run, "fewest runs");
+        int64_t next = 0;
+        for (size_t i = 0; i < runs.size(); ++i) {
+            const fsdp::SweepRun& r = runs[i];
+            CHECK(r.t_first == next && r.n_tiles >= 1, "runs contiguous");
+            CHECK(r.n_tiles <= runs[0].n_tiles && (i + 1 == runs.size() || r.n_tiles == runs[0].n_tiles),
+                  "runs of equal length, the last no longer");
+            CHECK(r.n_single == r.n_tiles % kv, "single tiles");
+            CHECK(r.cut == ((i + 1 == runs.size() && cut) ? 1 : 0), "cut tile only in the last run");
+            CHECK(r.blocks == r.cut + r.n_single + r.n_tiles / kv && r.blocks <= cap &&
+                      r.blocks < (int64_t(1) << 31), "grid fits");
+            next += r.n_tiles;
+        }
+        CHECK(next == tiles, "every whole tile once");
+    }
+}
+
 }  // namespace
 
 int main(int argc, char** argv) {
@@ -241,6 +274,7 @@ int main(int argc, char** argv) {
         check_unit(u, fsdp::kRows, N, rng);
     }
     check_overflow();
+    check_sweep_runs(rng, 20 * iters);
     if (g_fail) {
         std::fprintf(stderr, "%d failures\n", g_fail);
         return 1;
