@@ -19,18 +19,17 @@
  *     e.g. a torch CUDA tensor's data_ptr()).  Tables of device pointers
  *     (`params`, `outs`, `contribs`) are HOST arrays whose entries are device
  *     pointers; the library reads the host array during the call only.
- *   - The caller owns every buffer.  The four data calls allocate nothing,
- *     free nothing and do not synchronise: they enqueue kernels on `stream`
- *     (a hipStream_t; NULL is the default stream) and return.  Buffers must
- *     stay alive until that work has finished.
+ *   - The caller owns every buffer.  The data calls allocate no device
+ *     memory, free nothing and do not synchronise: they enqueue kernels on
+ *     `stream` (a hipStream_t; NULL is the default stream) and return.
+ *     Buffers must stay alive until that work has finished.
  *   - Errors: every argument is validated on the host, before any HIP call;
  *     a call that returns any status but FSDP_OK or FSDP_E_HIP has launched
  *     nothing and written nothing.  FSDP_E_HIP means a launch failed
  *     (hipGetLastError); a call that launches several kernels may have
- *     enqueued the ones before it.  Faults
- *     inside kernels surface at the caller's next synchronisation, as for any
- *     HIP work.  fsdp_last_error() returns a message for the calling thread's
- *     last non-OK status.
+ *     enqueued the ones before it.  Faults inside kernels surface at the
+ *     caller's next synchronisation, as for any HIP work.  fsdp_last_error()
+ *     returns a message for the calling thread's last non-OK status.
  *   - Pointer alignment is not an error: data at least 4-byte aligned is read
  *     with 16-byte loads where it sits (a scalar head first aligns outputs),
  *     and bf16 data at odd element offsets is realigned in the kernels.
@@ -160,14 +159,16 @@ FSDP_API fsdp_status fsdp_unit_create(int32_t layout, int32_t n_params, const in
 
 /* Free a unit.  Work already enqueued does not use the unit (every call copies
  * what its kernels need into their arguments), so no synchronisation is
- * needed first.  NULL is accepted. */
+ * needed first.  NULL is accepted.  Always returns FSDP_OK. */
 FSDP_API fsdp_status fsdp_unit_destroy(fsdp_unit* unit);
 
-/* Sizes of the unit, and of rank k's shard (k in [0,N) or FSDP_ALL_RANKS). */
+/* Sizes of the unit, and of rank k's shard (k in [0,N) or FSDP_ALL_RANKS).
+ * Host only.  Errors: FSDP_E_ARG (NULL unit or out), FSDP_E_RANGE (k). */
 FSDP_API fsdp_status fsdp_unit_info(const fsdp_unit* unit, int32_t k, fsdp_unit_sizes* out);
 
 /* Element offset of parameter i inside the FLAT flat buffer, or inside every
- * rank's ROWS segment (the q_i of FSDP_ROWS). */
+ * rank's ROWS segment (the q_i of FSDP_ROWS).  Host only.  Errors: FSDP_E_ARG
+ * (NULL unit or offset), FSDP_E_RANGE (i outside [0, n_params)). */
 FSDP_API fsdp_status fsdp_unit_param_offset(const fsdp_unit* unit, int32_t i, int64_t* offset);
 
 /* Recommended row pitch, in elements, of a stacked [N][pitch] bf16 buffer that

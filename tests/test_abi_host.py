@@ -581,6 +581,17 @@ def test_documented_error_statuses(B):
         (lambda: lib.fsdp_grad_accumulate(h, 0, FAKE, None, 1, None), "FSDP_E_ARG"),
         (lambda: lib.fsdp_grad_accumulate(h, -3, FAKE, FAKE, 1, None), "FSDP_E_RANGE"),
         (lambda: lib.fsdp_grad_accumulate(h, 0, FAKE + 1, FAKE, 1, None), "FSDP_E_ALIGN"),
+        # plan queries
+        (lambda: lib.fsdp_unit_info(None, 0, ctypes.byref(B.fsdp_unit_sizes())), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unit_info(h, 0, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unit_info(h, 4, ctypes.byref(B.fsdp_unit_sizes())), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_unit_param_offset(None, 0, ctypes.byref(ctypes.c_int64())), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unit_param_offset(h, 0, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unit_param_offset(h, 2, ctypes.byref(ctypes.c_int64())), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_unit_param_offset(h, -1, ctypes.byref(ctypes.c_int64())), "FSDP_E_RANGE"),
+        (lambda: lib.fsdp_unit_recv_pitch(None, ctypes.byref(ctypes.c_int64())), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unit_recv_pitch(h, None), "FSDP_E_ARG"),
+        (lambda: lib.fsdp_unit_destroy(None), "FSDP_OK"),
     ]
     for i, (call, want) in enumerate(cases):
         got = B.STATUS_NAMES.get(call(), "?")
