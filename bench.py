@@ -96,17 +96,20 @@ def kernel_src_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def load_traffic(per_launch_bytes_expected):
-    """HBM bytes per copy-out launch from the committed rocprofv3 counter summary, or None
-    when there is none or the kernel source changed since it was taken."""
+def load_traffic(workload, N, k, contribs):
+    """HBM bytes (read + write) per launch of each kernel, from the committed rocprofv3 counter
+    summary, or {} when there is none, it was taken on another workload (unit, N, rank, layout
+    of the contributions) or the kernel source changed since it was taken."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
-        return None
+        return {}
     if t.get("kernel_src_sha256") != kernel_src_hash():
-        return None
-    return t.get("copyout_hbm_bytes_per_launch")
+        return {}
+    if t.get("bench_args") != {"workload": workload, "N": N, "rank": k, "contribs": contribs}:
+        return {}
+    return {n: v["read_bytes"] + v["write_bytes"] for n, v in t.get("per_kernel", {}).items()}
 
 
 def time_stats(ms):
@@ -411,6 +414,7 @@ def main():
     # with flushing the fills sit between the kernels, so the step is the kernels' sum
     ms_step = sum(ms_k.values()) if flush_on else wall * 1e3 / args.steps
     step_bytes = sum(bytes_k.values())
+    traffic = load_traffic(args.workload, N, k, args.contribs)
     kernels = {}
     for n in order:
         gbs = bytes_k[n] / (ms_k[n] * 1e-3) / 1e9
@@ -418,13 +422,13 @@ def main():
         kernels[n] = {"ms": round(ms_k[n], 4), "bytes": bytes_k[n], "GB/s": round(gbs, 1),
                       "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
                       "elements_per_s": float("%.4g" % (elems_k[n] / (ms_k[n] * 1e-3))),
-                      "ms_median": round(med, 4), "ms_min": round(lo, 4), "ms_p90": round(p90, 4)}
+                      "ms_median": round(med, 4), "ms_min": round(lo, 4), "ms_p90": round(p90, 4),
+                      "traffic": traffic.get(n)}
     kernels["grad_reduce"]["input_elements_per_s"] = float(
         "%.4g" % (N * S / (ms_k["grad_reduce"] * 1e-3)))
 
     dom = max(order, key=lambda n: ms_k[n])
     achieved = bytes_k[dom] / (ms_k[dom] * 1e-3) / 1e9
-    traffic = load_traffic(bytes_k["copyout"]) if dom == "copyout" else None
     result = {
         "metric": METRIC,
         "value": round(step_bytes / (ms_step * 1e-3) / 1e9, 1),
@@ -453,7 +457,7 @@ def main():
                           "AdamW); rocprofv3 kernel durations are in profiles/"),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic.get(dom)},
     }
 
     use_graph = args.graph == "on" or (args.graph == "auto" and not flush_on)
