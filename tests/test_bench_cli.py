@@ -36,3 +36,25 @@ def test_traffic_is_reported_only_for_the_profiled_workload_and_source():
     assert bench.load_traffic("gpt175b", 120, 59, "pitched") == {}
     assert bench.load_traffic("gpt175b", 128, 63, "stacked") == {}
     assert bench.load_traffic("t5", 128, 63, "pitched") == {}
+
+
+def test_mean_split_and_time_statistics():
+    """The mean over N ranks is split into pre * post = N with pre = 2^floor(floor(log2 N) / 2),
+    the power of two with pre^2 <= N < 4 pre^2; kernel times report the nearest-rank median and
+    p90."""
+    import bench
+    assert bench.pre_post(1) == (1.0, 1.0)
+    assert bench.pre_post(3) == (1.0, 3.0)
+    assert bench.pre_post(4) == (2.0, 2.0)
+    assert bench.pre_post(8) == (2.0, 4.0)
+    assert bench.pre_post(128) == (8.0, 16.0)
+    assert bench.pre_post(120) == (8.0, 15.0)
+    for n in range(1, 300):
+        pre, post = bench.pre_post(n)
+        assert pre * post == n and pre == 2.0 ** ((n.bit_length() - 1) // 2)
+        assert pre * pre <= n < 4 * pre * pre
+    assert bench.time_stats([3.0]) == (3.0, 3.0, 3.0, 3.0)
+    assert bench.time_stats([4.0, 1.0, 3.0, 2.0]) == (2.5, 2.5, 1.0, 4.0)
+    ms = [float(v) for v in range(10, 0, -1)]
+    mean, med, lo, p90 = bench.time_stats(ms)
+    assert (mean, med, lo, p90) == (5.5, 5.5, 1.0, 9.0)
