@@ -11,7 +11,9 @@
 //     (a grid-stride version of the same copy runs ~20% slower).  The one
 //     exception is the many-rank reduction's sweep (below): there the window
 //     that matters is over ranks, and a longer run per wave keeps it compact;
-//   - outputs stored non-temporally (streamed, never re-read by the kernel).
+//   - outputs stored non-temporally (streamed, never re-read by the kernel); the
+//     copies' whole tiles with device-scope nt buffer stores, which stream out
+//     faster than the default-scope ones (the in-place kernels keep the latter).
 // The kernels:
 //   - segcopy: one engine for flatten (FSDP1 and FSDP2), copy-out, the cast and
 //     the bf16 copies.  The host planner turns the layout into a short table of
@@ -88,6 +90,15 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #ifndef FSDP_SWEEP_MIN_TILES
 #define FSDP_SWEEP_MIN_TILES 12288  // and from this many whole 512-output tiles on
 #endif
+#ifndef FSDP_TILE_STORE_CPOL
+// Whole-tile stores of the copies: 0 = global nt stores, else the cache-policy operand of
+// buffer stores (2 nt, 16 sc1 = device scope, 18 both).  Device-scope nt stores (18) against
+// global nt stores on the GPT-175B unit (HIP events, alternating processes on one box):
+// copy-out 6.48-6.50 vs 6.44-6.45 TB/s, rank flatten 5.26-5.39 vs 4.87-4.94, bf16 copies
+// 6.65-6.69 vs 6.24-6.30; buffer nt stores (2) matched the global ones, and sc1 alone slowed
+// the next kernel (AdamW) by a third.
+#define FSDP_TILE_STORE_CPOL 18
+#endif
 #ifndef FSDP_ACC_VPL
 #define FSDP_ACC_VPL 4          // 4-element vectors per lane in the local accumulation (1/2/4: 5.70/5.96/6.07 TB/s)
 #endif
@@ -105,6 +116,13 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #endif
 #ifndef FSDP_ADAM_NT_STORE
 #define FSDP_ADAM_NT_STORE 1  // and streams p, m, v back with nt stores
+#endif
+#ifndef FSDP_ADAM_STORE_CPOL
+// AdamW's whole-block stores: 0 = global stores (nt as FSDP_ADAM_NT_STORE says), else buffer
+// stores with this cache-policy operand.  Buffer nt stores (2) measured 6.62-6.65 TB/s against
+// 6.48-6.55 for global nt stores; device-scope nt stores (18) 5.46-5.59.  Those also slowed
+// the in-place accumulation and unscale, which keep global stores.
+#define FSDP_ADAM_STORE_CPOL 2
 #endif
 
 constexpr int kThreads = FSDP_COPY_THREADS;
@@ -166,11 +184,32 @@ __device__ __forceinline__ uint16_t to_bf16(float a) {
     return static_cast<uint16_t>(pack_bf16x2(a, 0.0f) & 0xFFFFu);
 }
 
+// Buffer stores of whole blocks.  The resource spans `bytes` from `base`, an address that is
+// the same in every lane (taken from the first active lane, so the resource sits in scalar
+// registers); word 3 holds the 32-bit data format CDNA's buffer instructions need.  Callers
+// store only at offsets inside the block, so the range check never drops a store.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(void* base, int bytes) {
+    const uint64_t b = reinterpret_cast<uintptr_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(
+        reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0, bytes, 0x00020000);
+}
+template <int kCpol>
+__device__ __forceinline__ void bst4(__amdgpu_buffer_rsrc_t r, int off, f4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, kCpol);
+}
+template <int kCpol>
+__device__ __forceinline__ void bst2(__amdgpu_buffer_rsrc_t r, int off, u2 v) {
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kCpol);
+}
+
 // Element pipes of the copy engine.  A vector is one 16-byte source load (4 fp32
 // or 8 bf16) and one store of the same element count (16 bytes, or 8 bytes for
 // fp32 -> bf16); `gather` re-reads a bf16 vector from LDS at an element shift.  kVpl vectors per lane make a tile of kThreads * E * kVpl
 // elements, lane l owning vectors l, l + kThreads, ... so every load and store
-// instruction is contiguous across the wave.
+// instruction is contiguous across the wave.  `put_tile` stores a whole tile from
+// its first element, which every lane of the workgroup shares.
 template <typename SrcT, typename DstT> struct Cp;
 template <> struct Cp<float, float> {
     static constexpr int E = 4, kVpl = FSDP_F32_VPL;
@@ -179,6 +218,17 @@ template <> struct Cp<float, float> {
     __device__ static V load(const float* p) { return ld4(p); }
     __device__ static V loadw(const float* p) { return ld4w(p); }
     __device__ static void put(float* d, V x) { st4(d, x); }
+    __device__ static void put_tile(float* d, const V* x) {
+#if FSDP_TILE_STORE_CPOL
+        const auto r = block_rsrc(d, kThreads * E * kVpl * 4);
+#pragma unroll
+        for (int u = 0; u < kVpl; ++u)
+            bst4<FSDP_TILE_STORE_CPOL>(r, 16 * (threadIdx.x + u * kThreads), x[u]);
+#else
+#pragma unroll
+        for (int u = 0; u < kVpl; ++u) put(d + E * (threadIdx.x + u * kThreads), x[u]);
+#endif
+    }
     __device__ static void put1(float* d, float x) { *d = x; }
     __device__ static void zero(float* d) { st4(d, f4{0.0f, 0.0f, 0.0f, 0.0f}); }
     __device__ static void zero1(float* d) { *d = 0.0f; }
@@ -191,6 +241,18 @@ template <> struct Cp<float, uint16_t> {
     __device__ static V loadw(const float* p) { return ld4w(p); }
     __device__ static void put(uint16_t* d, V x) {
         stu2(d, u2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
+    }
+    __device__ static void put_tile(uint16_t* d, const V* x) {
+#if FSDP_TILE_STORE_CPOL
+        const auto r = block_rsrc(d, kThreads * E * kVpl * 2);
+#pragma unroll
+        for (int u = 0; u < kVpl; ++u)
+            bst2<FSDP_TILE_STORE_CPOL>(r, 8 * (threadIdx.x + u * kThreads),
+                                       u2{pack_bf16x2(x[u][0], x[u][1]), pack_bf16x2(x[u][2], x[u][3])});
+#else
+#pragma unroll
+        for (int u = 0; u < kVpl; ++u) put(d + E * (threadIdx.x + u * kThreads), x[u]);
+#endif
     }
     __device__ static void put1(uint16_t* d, float x) { *d = to_bf16(x); }
     __device__ static void zero(uint16_t* d) { stu2(d, u2{0u, 0u}); }
@@ -207,6 +269,18 @@ template <> struct Cp<uint16_t, uint16_t> {
                   p[4] | (uint32_t{p[5]} << 16), p[6] | (uint32_t{p[7]} << 16)};
     }
     __device__ static void put(uint16_t* d, V x) { stu4(d, x); }
+    __device__ static void put_tile(uint16_t* d, const V* x) {
+#if FSDP_TILE_STORE_CPOL
+        const auto r = block_rsrc(d, kThreads * E * kVpl * 2);
+#pragma unroll
+        for (int u = 0; u < kVpl; ++u)
+            bst4<FSDP_TILE_STORE_CPOL>(r, 16 * (threadIdx.x + u * kThreads),
+                                       __builtin_bit_cast(f4, x[u]));
+#else
+#pragma unroll
+        for (int u = 0; u < kVpl; ++u) put(d + E * (threadIdx.x + u * kThreads), x[u]);
+#endif
+    }
     __device__ static void put1(uint16_t* d, uint16_t x) { *d = x; }
     __device__ static void zero(uint16_t* d) { stu4(d, u4{0u, 0u, 0u, 0u}); }
     __device__ static void zero1(uint16_t* d) { *d = 0; }
@@ -243,8 +317,7 @@ __device__ __forceinline__ void tile_aligned(const SrcT* __restrict__ s, DstT* _
         typename P::V x[kVpl];
 #pragma unroll
         for (int u = 0; u < kVpl; ++u) x[u] = load(s + E * (threadIdx.x + u * kThreads));
-#pragma unroll
-        for (int u = 0; u < kVpl; ++u) P::put(d + E * (threadIdx.x + u * kThreads), x[u]);
+        P::put_tile(d, x);
         return;
     }
     for (int v = threadIdx.x; v < nv; v += kThreads) P::put(d + E * v, load(s + E * v));
@@ -823,6 +896,21 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
                     v[h][q] = vv;
                 }
             }
+#if FSDP_ADAM_STORE_CPOL
+            const auto rp = block_rsrc(a.p + base, kPerBlk * 4), rm = block_rsrc(a.m + base, kPerBlk * 4),
+                       rv = block_rsrc(a.v + base, kPerBlk * 4);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int o = 16 * (threadIdx.x + h * kAdamThreads);
+                bst4<FSDP_ADAM_STORE_CPOL>(rp, o, p[h]);
+                bst4<FSDP_ADAM_STORE_CPOL>(rm, o, m[h]);
+                bst4<FSDP_ADAM_STORE_CPOL>(rv, o, v[h]);
+                if constexpr (kBf16)
+                    bst2<FSDP_ADAM_STORE_CPOL>(block_rsrc(a.pb + base, kPerBlk * 2), o / 2,
+                                                 u2{pack_bf16x2(p[h][0], p[h][1]),
+                                                    pack_bf16x2(p[h][2], p[h][3])});
+            }
+#else
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int64_t o = base + 4 * (threadIdx.x + h * kAdamThreads);
@@ -832,6 +920,7 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
                 if constexpr (kBf16)
                     stu2(a.pb + o, u2{pack_bf16x2(p[h][0], p[h][1]), pack_bf16x2(p[h][2], p[h][3])});
             }
+#endif
             return;
         }
     }
