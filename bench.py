@@ -455,6 +455,7 @@ def main():
         "kernel_timing": ("HIP events recorded around each launch on its stream in the eager loop; "
                           "an event pair adds 2-5 us, a few percent on the short kernels (flatten, "
                           "AdamW); rocprofv3 kernel durations are in profiles/"),
+        "kernel_src_sha256": kernel_src_hash(),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic.get(dom)},

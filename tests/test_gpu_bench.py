@@ -52,6 +52,8 @@ def test_bench_json_line_on_the_tiny_unit():
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    import bench
+    assert d["kernel_src_sha256"] == bench.kernel_src_hash()
     # the committed counter summary covers the GPT-175B unit only
     assert r["traffic"] is None and all(k["traffic"] is None for k in d["kernels"].values())
     c = d["cpu_baseline"]
