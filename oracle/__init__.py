@@ -19,18 +19,21 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "fsdp_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_BUILT = os.path.join(_HERE, "liboracle.so")
+# FSDP_ORACLE_LIB may name another build of fsdp_oracle.c to load instead; the test suite
+# loads copies with planted mistakes this way to check that the pins reject them.
+_LIB_PATH = os.environ.get("FSDP_ORACLE_LIB") or _BUILT
 
 CFLAGS = ["-O2", "-std=c99", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared"]
 
 
-def build(force: bool = True) -> str:
-    """Compile fsdp_oracle.c with gcc into oracle/liboracle.so."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", *CFLAGS, _SRC, "-o", tmp, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+def build(force: bool = True, src: str = _SRC, out: str = _BUILT) -> str:
+    """Compile fsdp_oracle.c (or another copy of it) with gcc into oracle/liboracle.so."""
+    if force or not os.path.exists(out):
+        tmp = out + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *CFLAGS, src, "-o", tmp, "-lm"])
+        os.replace(tmp, out)
+    return out
 
 
 _lib = None
@@ -44,6 +47,8 @@ def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
+            if _LIB_PATH != _BUILT:
+                raise FileNotFoundError("FSDP_ORACLE_LIB names a missing library: " + _LIB_PATH)
             build(force=False)
         lib = ctypes.CDLL(_LIB_PATH)
         lib.orc_bf16.argtypes = [ctypes.c_float]

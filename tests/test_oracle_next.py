@@ -140,14 +140,16 @@ def test_accumulate_integer_micro_batches_exact(orc):
     assert np.array_equal(acc, want.astype(np.float32))
 
 
-def test_accumulate_matches_sequential_fp32_addition(orc):
+@pytest.mark.parametrize("pre,post", [(2.0, 4.0), (3.0, 5.0)])
+def test_accumulate_matches_sequential_fp32_addition(orc, pre, post):
     """old + fresh is one binary32 addition: compare with numpy's float32 add (IEEE) of the
-    oracle's own non-accumulating result."""
+    oracle's own non-accumulating result.  With a post that is not a power of two this also
+    tells old + sum/post apart from (old*post + sum)/post, which rounds differently."""
     c = W.host_contribs(8, 5000, step=6)
     old = W.host_normal(5000, 1e-3, seed=3)
-    fresh = orc.grad_reduce_ex(list(c), 2.0, 4.0)
+    fresh = orc.grad_reduce_ex(list(c), pre, post)
     acc = old.copy()
-    orc.grad_reduce_ex(list(c), 2.0, 4.0, out=acc)
+    orc.grad_reduce_ex(list(c), pre, post, out=acc)
     assert np.array_equal(acc.view(np.uint32), (old + fresh).view(np.uint32))
 
 
