@@ -58,3 +58,20 @@ def test_mean_split_and_time_statistics():
     ms = [float(v) for v in range(10, 0, -1)]
     mean, med, lo, p90 = bench.time_stats(ms)
     assert (mean, med, lo, p90) == (5.5, 5.5, 1.0, 9.0)
+
+
+def test_committed_counter_traffic_matches_the_algorithmic_bytes():
+    """The committed PMC summary (GPT-175B block, N = 128, rank 63) shows every main kernel
+    reading and writing its algorithmic bytes to within 0.2%: no wasted re-reads."""
+    import json
+    import bench
+    with open(bench.TRAFFIC_FILE) as f:
+        t = json.load(f)
+    S, T = 14_157_024, 1_812_099_072
+    alg = {"copyout": (4 * T, 2 * T), "grad_reduce": (2 * 128 * S, 4 * S),
+           "adamw": (16 * S, 12 * S), "flatten": (4 * S, 4 * S)}
+    for name, (rd, wr) in alg.items():
+        k = t["per_kernel"][name]
+        assert abs(k["read_bytes"] / rd - 1) < 2e-3, (name, k["read_bytes"], rd)
+        assert abs(k["write_bytes"] / wr - 1) < 2e-3, (name, k["write_bytes"], wr)
+    assert t["copyout_hbm_bytes_per_launch"] == sum(t["per_kernel"]["copyout"].values())
