@@ -20,7 +20,8 @@
 //     (src, dst, length[, block stride]) segments passed in the kernel argument
 //     block; each workgroup takes one tile of one segment (the tile -> segment
 //     lookup is a wave-uniform binary search on scalar registers), so no lane
-//     ever searches and every tile is a straight streaming copy.  When source
+//     ever searches and every tile is a straight streaming copy.  Launches of
+//     2^18 tiles or more hand each XCD one contiguous run of tiles.  When source
 //     and destination are not 16-byte co-aligned, a scalar head aligns the
 //     destination and the source is read in place with dword-aligned 16-byte
 //     loads; only a bf16 source at an odd element offset is staged through LDS.
@@ -98,6 +99,14 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 // 6.65-6.69 vs 6.24-6.30; buffer nt stores (2) matched the global ones, and sc1 alone slowed
 // the next kernel (AdamW) by a third.
 #define FSDP_TILE_STORE_CPOL 18
+#endif
+#ifndef FSDP_XCD_MIN_TILES
+// From this many tiles (workgroups) on, a launch gives each of the eight XCDs one contiguous
+// run of tiles instead of every eighth tile.  Library fp32 copy, one box, alternating
+// processes: 8-32 MB equal, 64-256 MB 3-7% slower, 0.5-1 GB equal, 8.6 GB 1.5% faster; the
+// GPT-175B copy-out (885k tiles) 6.61-6.64 vs 6.46-6.49 TB/s.  The in-place local
+// accumulation measured 2% slower in this order, so it keeps the dispatch order.
+#define FSDP_XCD_MIN_TILES (1u << 18)
 #endif
 #ifndef FSDP_ACC_VPL
 #define FSDP_ACC_VPL 4          // 4-element vectors per lane in the local accumulation (1/2/4: 5.70/5.96/6.07 TB/s)
@@ -300,9 +309,20 @@ struct DevSeg {
 struct SegTable {
     uint32_t ntiles;
     uint32_t nseg;
+    uint32_t xcd_runs;  // tiles in XCD-contiguous order (xcd_contiguous)
+    uint32_t unused;
     DevSeg seg[kMaxSegs];
 };
 static_assert(sizeof(SegTable) <= 4096, "segment table must fit one kernel argument block");
+
+// The dispatcher deals a launch's workgroups to MI355X's eight XCDs in turn (workgroup b to
+// XCD b % 8).  This maps b to the tile it runs so that each XCD takes one contiguous run of
+// the G tiles (the first G % 8 XCDs one tile more).  It is a bijection of [0, G) whatever the
+// placement, so results never depend on it; only speed does.
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t G) {
+    const uint32_t x = b & 7u, loc = b >> 3, per = G >> 3, rem = G & 7u;
+    return x * per + (x < rem ? x : rem) + loc;
+}
 
 // n <= tile elements; s 16-byte aligned (kWord: 4-byte aligned), d aligned for its
 // vector store.
@@ -389,7 +409,7 @@ template <typename SrcT, typename DstT, bool kGeneral>
 __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable t) {
     constexpr int kTile = tile_elems<SrcT, DstT>();
     __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral && sizeof(SrcT) == 2 ? kTile + 16 : 8];
-    const uint32_t tile = blockIdx.x;
+    const uint32_t tile = t.xcd_runs ? xcd_contiguous(blockIdx.x, t.ntiles) : blockIdx.x;
     // wave-uniform lookup of the segment holding this tile
     uint32_t lo = 0, hi = t.nseg - 1;
     while (lo < hi) {
@@ -976,6 +996,7 @@ hipError_t launch_segcopy_t(const std::vector<CopySeg>& segs, hipStream_t stream
         }
         if (t.nseg == 0) continue;
         t.ntiles = static_cast<uint32_t>(tiles);
+        t.xcd_runs = tiles >= FSDP_XCD_MIN_TILES ? 1u : 0u;
         if (general)
             hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, true>), grid_of(tiles), dim3(kThreads),
                                0, stream, t);

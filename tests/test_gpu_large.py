@@ -143,3 +143,36 @@ def test_many_rank_sweep_over_a_shard_beyond_2_31_elements():
     cs = [to_host(c[r].view(torch.int16).index_select(0, ti)).view(np.uint16) for r in range(N)]
     assert_f32_tol_then_bits(to_host(out.index_select(0, ti)), oracle.grad_reduce(cs, 4.0, 8.0),
                              "sweep samples beyond 2^31")
+
+
+@pytest.mark.parametrize("rem", [0, 1, 3, 7])
+def test_xcd_ordered_launches_cover_every_tile_once(rem):
+    """Launches of at least 2^18 tiles run in XCD-contiguous order (each XCD one run of
+    tiles; the first G % 8 XCDs one more).  Here G = 2^18 + rem tiles of 1024 fp32 with a
+    ragged last tile and a segment boundary inside an XCD's run (two parameters, N = 1, so
+    the shard is the concatenation): every element must land once, bit for bit, and the
+    fp32 -> bf16 copy-out of the same layout (half as many tiles) must match torch's cast."""
+    tiles = (1 << 18) + rem
+    n = tiles * 1024 - 5
+    a_n = 37 * 1024 * 1024 + 11  # the boundary falls mid-tile, inside one XCD's run
+    shapes = [(a_n,), (n - a_n,)]
+    u = B.fsdp_unit_create(B.FSDP_FLAT, shapes, 1)
+    assert u.S == n
+    gen = torch.Generator(device=dev()).manual_seed(500 + rem)
+    params = [torch.randn(s, device=dev(), generator=gen) for s in shapes]
+    shard = torch.full((n,), float("nan"), device=dev())
+    B.fsdp_flatten_shard(u, params, 0, shard)
+    _sync()
+    assert _same_bits(shard, torch.cat(params)), rem
+    # copy-out: 2048-element tiles, so twice the size again crosses 2^18 tiles
+    big_n = 2 * n
+    u2 = B.fsdp_unit_create(B.FSDP_FLAT, [(big_n - a_n,), (a_n,)], 1)
+    g = torch.randn(big_n, device=dev(), generator=gen)
+    outs = [torch.empty(big_n - a_n, dtype=torch.bfloat16, device=dev()),
+            torch.empty(a_n, dtype=torch.bfloat16, device=dev())]
+    B.fsdp_unflatten_copyout(u2, g, outs)
+    _sync()
+    assert _same_bits(torch.cat(outs), g.to(torch.bfloat16)), rem
+    idx = _sample_idx(big_n, 600 + rem)
+    got = to_host(torch.cat(outs))[idx]
+    assert_bf16_bits(got, oracle.bf16(to_host(g)[idx]), "copy-out samples rem=%d" % rem)
