@@ -21,7 +21,7 @@
 //     block; each workgroup takes one tile of one segment (the tile -> segment
 //     lookup is a wave-uniform binary search on scalar registers), so no lane
 //     ever searches and every tile is a straight streaming copy.  Launches of
-//     2^18 tiles or more hand each XCD one contiguous run of tiles.  When source
+//     2^18 tiles or more hand each XCD runs of 256 consecutive tiles.  When source
 //     and destination are not 16-byte co-aligned, a scalar head aligns the
 //     destination and the source is read in place with dword-aligned 16-byte
 //     loads; only a bf16 source at an odd element offset is staged through LDS.
@@ -102,12 +102,17 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 #define FSDP_TILE_STORE_CPOL 18
 #endif
 #ifndef FSDP_XCD_MIN_TILES
-// From this many tiles (workgroups) on, a launch gives each of the eight XCDs one contiguous
-// run of tiles instead of every eighth tile.  Library fp32 copy, one box, alternating
-// processes: 8-32 MB equal, 64-256 MB 3-7% slower, 0.5-1 GB equal, 8.6 GB 1.5% faster; the
-// GPT-175B copy-out (885k tiles) 6.61-6.64 vs 6.46-6.49 TB/s.  The in-place local
-// accumulation measured 2% slower in this order, so it keeps the dispatch order.
+// From this many tiles (workgroups) on, a copy hands each of the eight XCDs runs of
+// FSDP_XCD_CHUNK consecutive tiles instead of every eighth tile.  GPT-175B copy-out (885k
+// tiles), one box, alternating processes: dispatch order 6.46-6.49 TB/s, one contiguous run
+// per XCD 6.61-6.65, runs of 64 / 128 / 256 / 512 tiles 6.65-6.67 / 6.76 / 6.76-6.78 /
+// 6.62-6.63.  One run per XCD made 64-256 MB copies 3-7% slower; runs of 256 left every
+// size from 8 MB to 1 GB as fast as the dispatch order.  The in-place local accumulation
+// measured 2% slower with one run per XCD, so it keeps the dispatch order.
 #define FSDP_XCD_MIN_TILES (1u << 18)
+#endif
+#ifndef FSDP_XCD_CHUNK
+#define FSDP_XCD_CHUNK 256u
 #endif
 #ifndef FSDP_ACC_VPL
 #define FSDP_ACC_VPL 4          // 4-element vectors per lane in the local accumulation (1/2/4: 5.70/5.96/6.07 TB/s)
@@ -310,7 +315,7 @@ struct DevSeg {
 struct SegTable {
     uint32_t ntiles;
     uint32_t nseg;
-    uint32_t xcd_runs;  // tiles in XCD-contiguous order (xcd_contiguous)
+    uint32_t xcd_runs;  // tiles in XCD-chunked order (xcd_chunked)
     uint32_t unused;
     DevSeg seg[kMaxSegs];
 };
@@ -323,6 +328,18 @@ static_assert(sizeof(SegTable) <= 4096, "segment table must fit one kernel argum
 __device__ __forceinline__ uint32_t xcd_contiguous(uint32_t b, uint32_t G) {
     const uint32_t x = b & 7u, loc = b >> 3, per = G >> 3, rem = G & 7u;
     return x * per + (x < rem ? x : rem) + loc;
+}
+
+// The same in groups of 8 C tiles: inside each group XCD x takes the C tiles from x C on, so
+// the eight XCDs work through one compact window of the launch; a last, partial group is
+// split by xcd_contiguous.  Also a bijection of [0, G).
+template <uint32_t C>
+__device__ __forceinline__ uint32_t xcd_chunked(uint32_t b, uint32_t G) {
+    constexpr uint32_t span = 8u * C;
+    const uint32_t full = G / span * span;
+    if (b >= full) return full + xcd_contiguous(b - full, G - full);
+    const uint32_t r = b % span;
+    return b - r + (r & 7u) * C + (r >> 3);
 }
 
 // n <= tile elements; s 16-byte aligned (kWord: 4-byte aligned), d aligned for its
@@ -410,7 +427,8 @@ template <typename SrcT, typename DstT, bool kGeneral>
 __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable t) {
     constexpr int kTile = tile_elems<SrcT, DstT>();
     __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral && sizeof(SrcT) == 2 ? kTile + 16 : 8];
-    const uint32_t tile = t.xcd_runs ? xcd_contiguous(blockIdx.x, t.ntiles) : blockIdx.x;
+    const uint32_t tile =
+        t.xcd_runs ? xcd_chunked<FSDP_XCD_CHUNK>(blockIdx.x, t.ntiles) : blockIdx.x;
     // wave-uniform lookup of the segment holding this tile
     uint32_t lo = 0, hi = t.nseg - 1;
     while (lo < hi) {

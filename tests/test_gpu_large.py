@@ -145,13 +145,15 @@ def test_many_rank_sweep_over_a_shard_beyond_2_31_elements():
                              "sweep samples beyond 2^31")
 
 
-@pytest.mark.parametrize("rem", [0, 1, 3, 7])
+@pytest.mark.parametrize("rem", [0, 1, 3, 7, 2047])
 def test_xcd_ordered_launches_cover_every_tile_once(rem):
-    """Launches of at least 2^18 tiles run in XCD-contiguous order (each XCD one run of
-    tiles; the first G % 8 XCDs one more).  Here G = 2^18 + rem tiles of 1024 fp32 with a
-    ragged last tile and a segment boundary inside an XCD's run (two parameters, N = 1, so
-    the shard is the concatenation): every element must land once, bit for bit, and the
-    fp32 -> bf16 copy-out of the same layout (half as many tiles) must match torch's cast."""
+    """Launches of at least 2^18 tiles run in XCD-chunked order (in each group of 8 x 256
+    tiles every XCD takes 256 consecutive ones; a partial last group is split evenly, the
+    first G % 8 XCDs one tile more).  Here G = 2^18 + rem tiles of 1024 fp32 (rem = 2047: a
+    partial group of 2047) with a ragged last tile and a segment boundary inside an XCD's run
+    (two parameters, N = 1, so the shard is the concatenation): every element must land once,
+    bit for bit, and the fp32 -> bf16 copy-out of the same layout (2048-element tiles, so
+    about as many tiles) must match torch's cast."""
     tiles = (1 << 18) + rem
     n = tiles * 1024 - 5
     a_n = 37 * 1024 * 1024 + 11  # the boundary falls mid-tile, inside one XCD's run
