@@ -39,7 +39,8 @@
 //     than nt ones (6.5 vs 5.6 TB/s), and nt stores put its writes in HBM within
 //     its own launch (plain stores leave them dirty in the 256 MB Infinity Cache,
 //     which costs the next kernels, or AdamW itself once they outgrow it).
-//   - accumulate, unscale: elementwise in place, four 16-byte vectors per lane.
+//   - accumulate, unscale: elementwise in place, four 16-byte vectors per lane
+//     (a long accumulation hands each XCD runs of 64 blocks).
 //   - sqnorm: per-parameter sums of squares in binary64, one tile per workgroup
 //     into a workspace, then one workgroup per parameter, in fixed orders.
 // Every binary32 step is one IEEE operation, in the order the CPU oracle fixes;
@@ -107,12 +108,17 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 // tiles), one box, alternating processes: dispatch order 6.46-6.49 TB/s, one contiguous run
 // per XCD 6.61-6.65, runs of 64 / 128 / 256 / 512 tiles 6.65-6.67 / 6.76 / 6.76-6.78 /
 // 6.62-6.63.  One run per XCD made 64-256 MB copies 3-7% slower; runs of 256 left every
-// size from 8 MB to 1 GB as fast as the dispatch order.  The in-place local accumulation
-// measured 2% slower with one run per XCD, so it keeps the dispatch order.
+// size from 8 MB to 1 GB as fast as the dispatch order.
 #define FSDP_XCD_MIN_TILES (1u << 18)
 #endif
 #ifndef FSDP_XCD_CHUNK
 #define FSDP_XCD_CHUNK 256u
+#endif
+#ifndef FSDP_ACC_XCD_CHUNK
+// The in-place local accumulation over all L (442k blocks) takes runs of 64 blocks per XCD:
+// 6.09-6.12 vs 6.01-6.08 TB/s in dispatch order; runs of 16 / 32 / 256 blocks 5.88-5.95 /
+// 5.96-6.01 / 5.99-6.00, one run per XCD 5.94-5.95 (one box, alternating processes).
+#define FSDP_ACC_XCD_CHUNK 64u
 #endif
 #ifndef FSDP_ACC_VPL
 #define FSDP_ACC_VPL 4          // 4-element vectors per lane in the local accumulation (1/2/4: 5.70/5.96/6.07 TB/s)
@@ -840,7 +846,10 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(const uint16_t* __
                                                               int64_t len) {
     constexpr int kV = FSDP_ACC_VPL;
     constexpr int64_t kPerBlk = static_cast<int64_t>(kThreads) * 4 * kV;
-    const int64_t base = static_cast<int64_t>(blockIdx.x) * kPerBlk;
+    const uint32_t blk = gridDim.x >= FSDP_XCD_MIN_TILES
+                             ? xcd_chunked<FSDP_ACC_XCD_CHUNK>(blockIdx.x, gridDim.x)
+                             : blockIdx.x;
+    const int64_t base = static_cast<int64_t>(blk) * kPerBlk;
     if (kVec && base + kPerBlk <= len) {
         // lane l owns elements [4l, 4l+4) of each of the tile's kV slices of 4 * kThreads
         u2 x[kV];
