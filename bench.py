@@ -50,7 +50,9 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="gpt175b",
                     choices=["gpt175b", "t5", "gpt2l", "rows", "tiny"])
-    ap.add_argument("--rank", type=int, default=None, help="rank k (default: N/2 - 1)")
+    ap.add_argument("--rank", type=int, default=None,
+                    help="rank k of the headline step (default: the rank whose flatten the rank "
+                         "sweep measured slowest; N/2 - 1 with --no-sweep-ranks)")
     ap.add_argument("--ranks", type=int, default=None,
                     help="shard the unit over this many ranks instead of its own N")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -70,9 +72,10 @@ def parse_args():
                          "the step order alone does not guarantee it); with flushing, the step time "
                          "is the sum of the kernels' event times")
     ap.add_argument("--sweep-ranks", dest="sweep_ranks", action="store_true", default=True,
-                    help="(default) also time flatten, reduce and AdamW for every rank (N <= 8) or "
-                         "for ranks 0, 1, N/2-1, N-1, each launch after a 1 GiB read flush, and "
-                         "report the worst rank beside the headline rank (`per_rank`)")
+                    help="(default) first time flatten, reduce and AdamW for every rank (N <= 8) or "
+                         "for ranks 0, 1, N/2-1, N-1, each launch after a 1 GiB read flush "
+                         "(`per_rank`); the headline step then runs at the rank whose flatten was "
+                         "slowest (reduce and AdamW move the same bytes at every rank)")
     ap.add_argument("--no-sweep-ranks", dest="sweep_ranks", action="store_false",
                     help="skip the rank sweep")
     ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
@@ -84,10 +87,18 @@ def parse_args():
                     help="also time a plain 4 GiB fp32 copy through the library (N = 1 unit) "
                          "and hipMemcpy device-to-device, as copy ceilings")
     ap.add_argument("--floor-probe", action="store_true",
-                    help="also run the library's fp32 copy (flatten of a one-parameter unit, N = 1) "
-                         "at 8 MB .. 1 GB of traffic, 20 launches per size, each after a 1 GiB "
-                         "read: the fixed cost and rate of a cold-cache copy, for rocprofv3's "
-                         "kernel trace (the event times reported here include event overhead)")
+                    help="also split the flatten of one rank shard into what any kernel of its "
+                         "shape pays: an empty kernel with the flatten's grid and with one wave, "
+                         "a read-only, a write-only and a plain copy kernel over the shard's bytes "
+                         "(libfsdpprobe.so), beside the flatten of ranks 0, 1, N/2-1 and N-1; and "
+                         "run the library's fp32 copy (flatten of a one-parameter unit, N = 1) at "
+                         "8 MB .. 1 GB of traffic.  20 launches each, each after a 1 GiB read, for "
+                         "rocprofv3's kernel trace (the event times reported here include event "
+                         "overhead)")
+    ap.add_argument("--contention-probe", action="store_true",
+                    help="also time the reduction on the tile kernel and on the row-major sweep "
+                         "alone and while a stream of bf16 GEMMs (a backward pass's compute) runs "
+                         "on a second stream of the same priority")
     return ap.parse_args()
 
 
@@ -98,8 +109,10 @@ def kernel_src_hash() -> str:
 
 def load_traffic(workload, N, k, contribs):
     """HBM bytes (read + write) per launch of each kernel, from the committed rocprofv3 counter
-    summary, or {} when there is none, it was taken on another workload (unit, N, rank, layout
-    of the contributions) or the kernel source changed since it was taken."""
+    summary, or {} when there is none, it was taken on another workload (unit, N, layout of the
+    contributions) or the kernel source changed since it was taken.  The flatten's entry is the
+    one of rank k (the summary holds the swept ranks); the other kernels move the same bytes at
+    every rank."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -107,9 +120,13 @@ def load_traffic(workload, N, k, contribs):
         return {}
     if t.get("kernel_src_sha256") != kernel_src_hash():
         return {}
-    if t.get("bench_args") != {"workload": workload, "N": N, "rank": k, "contribs": contribs}:
+    if t.get("bench_args") != {"workload": workload, "N": N, "contribs": contribs}:
         return {}
-    return {n: v["read_bytes"] + v["write_bytes"] for n, v in t.get("per_kernel", {}).items()}
+    out = {n: v["read_bytes"] + v["write_bytes"] for n, v in t.get("per_kernel", {}).items()}
+    fl = t.get("flatten_by_rank", {}).get(str(k))
+    if fl is not None:
+        out["flatten"] = fl["read_bytes"] + fl["write_bytes"]
+    return out
 
 
 def time_stats(ms):
@@ -189,9 +206,120 @@ def cpu_baseline(host, unit, N, k, S, valid, pre, post, hp, rows):
         "sample": ("%s unit, N=%d, rank %d: flatten of the rank (whole), copy-out of the whole "
                    "unit, reduction of the first S/8=%d outputs over all %d ranks, AdamW on the "
                    "whole shard; single-threaded C oracle" % (unit.name, N, k, n_red, N)),
+        "cpu_model": host_cpu_model(),
         "per_kernel_gbs": {name: round(b / dt / 1e9, 3) for name, (b, dt) in parts.items()},
         "seconds": round(t_tot, 2),
     }
+
+
+def _slices(n, parts):
+    """[a, b) bounds cutting range(n) into `parts` nearly equal pieces (empty ones dropped)."""
+    step = -(-n // parts) if n else 0
+    return [(a, min(n, a + step)) for a in range(0, n, step)] if n else []
+
+
+def _flat_pieces(params, numels, lo, hi):
+    """1-D pieces of the concatenated parameters covering flat elements [lo, hi)."""
+    out, off = [], 0
+    for p, n in zip(params, numels):
+        a, b = max(lo, off), min(hi, off + n)
+        if a < b:
+            out.append(p.reshape(-1)[a - off:b - off])
+        off += n
+    return out
+
+
+def host_cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline_all_cores(host, unit, N, k, S, valid, pre, post, hp, rows, threads):
+    """The same sample as cpu_baseline, with the unchanged single-threaded oracle run on
+    disjoint output slices by `threads` host threads at once (its C calls release the GIL;
+    every output element is independent, so results are those of one call): the flatten and
+    the copy-out of a FLAT unit cut into slices of the flat range (each slice's parameter
+    pieces flattened or cast as a unit of their own), the reduction and AdamW cut into slices
+    of the shard.  The rows layout's flatten and copy-out take whole parameters per thread."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
+    import oracle
+
+    parts = {}
+    numels = [int(np.prod(s)) if len(s) else 1 for s in unit.shapes]
+    T = sum(numels)
+    with ThreadPoolExecutor(max_workers=threads) as pool:
+        def run(jobs):
+            t0 = time.perf_counter()
+            for f in [pool.submit(j) for j in jobs]:
+                f.result()
+            return time.perf_counter() - t0
+
+        if rows:
+            groups = [list(range(i, len(unit.shapes), threads)) for i in range(threads)]
+            jobs = [lambda g=g: oracle.rows_shard([host["params"][i] for i in g], N, k)
+                    for g in groups if g]
+        else:
+            jobs = [lambda a=a, b=b: oracle.flat_shard(
+                _flat_pieces(host["params"], numels, k * S + a, k * S + b), 1, 0)
+                for a, b in _slices(min(S, max(0, T - k * S)), threads)]
+        parts["flatten"] = (4 * valid + 4 * S, run(jobs))
+
+        g = host["gathered"]
+        if rows:
+            # a parameter's rows sit in every rank's segment: one call per parameter group
+            jobs = [lambda: oracle.rows_copyout(unit.shapes, N, g)]
+        else:
+            jobs = [lambda a=a, b=b: oracle.flat_copyout(
+                [(x.size,) for x in _flat_pieces(host["params"], numels, a, b)], g[a:b])
+                for a, b in _slices(T, threads)]
+        parts["copyout"] = (6 * unit.total, run(jobs))
+
+        n_red = S // 8
+        c = host["contribs"]
+        jobs = [lambda a=a, b=b: oracle.grad_reduce([c[r, a:b] for r in range(N)], pre, post)
+                for a, b in _slices(n_red, threads)]
+        parts["grad_reduce"] = ((2 * N + 4) * n_red, run(jobs))
+
+        p = host["adam_p"].copy()
+        gg = host["adam_g"]
+        m = np.zeros(S, np.float32)
+        v = np.zeros(S, np.float32)
+        jobs = [lambda a=a, b=b: oracle.adamw(p[a:b], gg[a:b], m[a:b], v[a:b], step=1, **hp)
+                for a, b in _slices(S, threads)]
+        parts["adamw"] = (28 * S, run(jobs))
+
+    b_tot = sum(b for b, _ in parts.values())
+    t_tot = sum(t for _, t in parts.values())
+    return {
+        "value": round(b_tot / t_tot / 1e9, 3),
+        "unit": "GB/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": ("the single-core sample (%s unit, N=%d, rank %d), each part cut into disjoint "
+                   "output slices run by %d threads at once%s" % (
+                       unit.name, N, k, threads,
+                       "; the rows layout's copy-out on one thread" if rows else "")),
+        "per_kernel_gbs": {name: round(b / dt / 1e9, 3) for name, (b, dt) in parts.items()},
+        "seconds": round(t_tot, 2),
+        "cpu_model": host_cpu_model(),
+    }
+
+
+def host_threads():
+    """Host threads for the all-cores baseline: the cores this process may run on, at most 16
+    (one GPU's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
 
 
 def time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows, grad, outs,
@@ -304,6 +432,147 @@ def sweep_ranks(B, u, N, contrib_rows, pre, post, hp, params, grad, shard, adam_
     return out
 
 
+def _event_median(fn, stream, reps, before=None):
+    """Median of `reps` single launches of fn timed with an event pair on `stream` (ms)."""
+    import torch
+    ev = []
+    for _ in range(reps):
+        if before is not None:
+            before()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        ev.append((e0, e1))
+    torch.cuda.synchronize()
+    return time_stats([a.elapsed_time(b) for a, b in ev])[1]
+
+
+def flatten_floor(B, u, N, params, stream, dev, gen, reps=20):
+    """What any kernel of the flatten's shape pays, beside the flatten itself, each launch after a
+    1 GiB read: an empty kernel with the flatten's grid (one 256-thread workgroup per 1024
+    elements of the shard) and with one wave; a read-only kernel over the shard's bytes; a
+    write-only one; a plain copy (loads, then device-scope nt stores, no segment table); then the
+    flatten of ranks 0, 1, N/2-1 and N-1.  The cases run in this order, `reps` launches each, so
+    that rocprofv3's kernel trace can be split by order (the probes are kernels of their own)."""
+    import ctypes
+    import torch
+    from sharded_fsdp_flatten_amd import build as lib_build
+    if not os.path.exists(lib_build.PROBE_LIB_PATH):
+        raise RuntimeError("libfsdpprobe.so is not built; run __graft_entry__.build()")
+    P = ctypes.CDLL(lib_build.PROBE_LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    P.fsdp_probe_empty.argtypes = [i64, i32, vp]
+    P.fsdp_probe_read.argtypes = [vp, i64, vp, vp]
+    P.fsdp_probe_write.argtypes = [vp, i64, vp]
+    P.fsdp_probe_copy.argtypes = [vp, vp, i64, vp]
+    S = u.info(0)["S"]
+    n = S // 4 * 4
+    tiles = -(-S // 1024)
+    src = torch.randn(S, device=dev, generator=gen)
+    dst = torch.empty(S, device=dev)
+    sink = torch.zeros(4, device=dev)
+    shard = torch.empty(S, device=dev)
+    fb = torch.zeros(1 << 28, device=dev)
+    fs = torch.zeros((), device=dev)
+    sp = stream.cuda_stream
+
+    def flush():
+        torch.sum(fb, dim=0, out=fs)
+
+    def probe(rc):
+        if rc != 0:
+            raise RuntimeError("probe launch failed (code %d)" % rc)
+
+    ks = sorted({0, 1, max(0, N // 2 - 1), N - 1})
+    cases = [
+        ("empty kernel, flatten grid (%d x 256)" % tiles, 0, lambda: probe(P.fsdp_probe_empty(tiles, 256, sp))),
+        ("empty kernel, one wave", 0, lambda: probe(P.fsdp_probe_empty(1, 64, sp))),
+        ("read only (%d fp32)" % n, 4 * n, lambda: probe(P.fsdp_probe_read(src.data_ptr(), n, sink.data_ptr(), sp))),
+        ("write only (%d fp32)" % n, 4 * n, lambda: probe(P.fsdp_probe_write(dst.data_ptr(), n, sp))),
+        ("copy (%d fp32)" % n, 8 * n, lambda: probe(P.fsdp_probe_copy(src.data_ptr(), dst.data_ptr(), n, sp))),
+    ]
+    for k in ks:
+        valid = u.info(k)["valid"]
+        cases.append(("flatten rank %d" % k, 4 * valid + 4 * S,
+                      lambda k=k: B.fsdp_flatten_shard(u, params, k, shard)))
+    out = {"S": S, "reps": reps, "order": [c[0] for c in cases], "cases": {}}
+    for name, nbytes, fn in cases:
+        fn()
+        med = _event_median(fn, stream, reps, before=flush)
+        row = {"event_ms_median": round(med, 5), "bytes": nbytes}
+        if nbytes:
+            row["GB/s"] = round(nbytes / (med * 1e-3) / 1e9, 1)
+        out["cases"][name] = row
+        print("flatten floor: %s done" % name, file=sys.stderr, flush=True)
+    del src, dst, sink, shard, fb
+    return out
+
+
+def contention_probe(B, u, N, contrib_rows, pre, post, grad, stream, dev, reps=10):
+    """The reduction on the tile kernel and on the row-major sweep, alone and overlapped with a
+    stream of bf16 GEMMs on a second stream of the same priority (the backward compute that the
+    ReduceScatter overlaps).  Per case: the reduction's duration (events on its stream), the
+    GEMM batch's duration, and the wall time until both are done."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    side = torch.cuda.Stream(device=dev)
+    gemms = 8
+
+    def gemm_batch():
+        with torch.cuda.stream(side):
+            for _ in range(gemms):
+                torch.matmul(a, b, out=c)
+
+    def reduce(kernel):
+        B.fsdp_grad_reduce_shard_ex(u, contrib_rows, pre, post, grad, kernel=kernel)
+
+    for kernel in ("tiles", "sweep"):
+        reduce(kernel)
+    gemm_batch()
+    torch.cuda.synchronize()
+    out = {"gemm": "%d bf16 matmuls %dx%dx%d on a second stream" % (gemms, n, n, n), "reps": reps}
+    e = {k: torch.cuda.Event(enable_timing=True) for k in ("g0", "g1", "r0", "r1")}
+    # the GEMM batch alone
+    ts = []
+    for _ in range(reps):
+        e["g0"].record(side)
+        gemm_batch()
+        e["g1"].record(side)
+        torch.cuda.synchronize()
+        ts.append(e["g0"].elapsed_time(e["g1"]))
+    out["gemm_alone_ms"] = round(time_stats(ts)[1], 4)
+    for kernel in ("tiles", "sweep"):
+        alone = _event_median(lambda: reduce(kernel), stream, reps)
+        red, gem, wall = [], [], []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            e["g0"].record(side)
+            gemm_batch()
+            e["g1"].record(side)
+            # the reduction starts once the GEMMs hold the device
+            stream.wait_event(e["g0"])
+            e["r0"].record(stream)
+            reduce(kernel)
+            e["r1"].record(stream)
+            torch.cuda.synchronize()
+            wall.append((time.perf_counter() - t0) * 1e3)
+            red.append(e["r0"].elapsed_time(e["r1"]))
+            gem.append(e["g0"].elapsed_time(e["g1"]))
+        out[kernel] = {"reduce_alone_ms": round(alone, 4),
+                       "reduce_overlapped_ms": round(time_stats(red)[1], 4),
+                       "gemm_overlapped_ms": round(time_stats(gem)[1], 4),
+                       "both_done_wall_ms": round(time_stats(wall)[1], 4)}
+        print("contention: %s done" % kernel, file=sys.stderr, flush=True)
+    del a, b, c
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -330,7 +599,7 @@ def main():
     layout = B.FSDP_FLAT if unit.layout == W.FLAT else B.FSDP_ROWS
     u = B.fsdp_unit_create(layout, unit.shapes, N)
     info = u.info(k)
-    S, L, T, valid = info["S"], info["L"], info["T"], info["valid"]
+    S, L, T = info["S"], info["L"], info["T"]
     pre, post = pre_post(N)
     hp = dict(unit.adam)
 
@@ -363,6 +632,20 @@ def main():
     def flush():
         torch.sum(flush_buf, dim=0, out=flush_sum)
 
+    stream = torch.cuda.current_stream()
+    # the rank sweep first: the headline step runs at its slowest flatten rank
+    per_rank = None
+    if args.sweep_ranks:
+        per_rank = sweep_ranks(B, u, N, contrib_rows, pre, post, hp, params, grad, shard, adam_p,
+                               m, v, stream, flush)
+        print("rank sweep done", file=sys.stderr, flush=True)
+        if args.rank is None:
+            k = per_rank["worst"]["flatten"]["rank"]
+    rank_choice = ("given (--rank)" if args.rank is not None
+                   else "the rank whose flatten the sweep measured slowest" if per_rank
+                   else "N/2 - 1 (no rank sweep)")
+    valid = u.info(k)["valid"]
+
     bytes_k = {
         "grad_reduce": (2 * N + 4) * S,
         "copyout": 6 * T,
@@ -371,7 +654,6 @@ def main():
     }
     elems_k = {"grad_reduce": S, "copyout": T, "adamw": S, "flatten": S}
     order = ["grad_reduce", "copyout", "adamw", "flatten"]
-    stream = torch.cuda.current_stream()
     step_no = [0]
 
     def run(name):
@@ -446,7 +728,8 @@ def main():
                                "N=%d, rank %d" % (unit.name, len(unit.shapes), T,
                                                   "FSDP1 flat" if layout == B.FSDP_FLAT
                                                   else "FSDP2 dim-0 row", N, k),
-                   "N": N, "rank": k, "S": S, "T": T, "pre_divide": pre, "post_divide": post,
+                   "N": N, "rank": k, "rank_choice": rank_choice, "S": S, "T": T,
+                   "pre_divide": pre, "post_divide": post,
                    "contribs": args.contribs if args.contribs == "separate"
                    else "%s (one buffer, row pitch %d elements)" % (args.contribs, pitch),
                    "step_time": ("sum of the kernels' event times, 1 GiB read before each kernel"
@@ -503,9 +786,8 @@ def main():
                                              grad, outs, gathered, adam_p, stream,
                                              flush if flush_on else None)
 
-    if args.sweep_ranks:
-        result["per_rank"] = sweep_ranks(B, u, N, contrib_rows, pre, post, hp, params, grad, shard,
-                                         adam_p, m, v, stream, flush)
+    if per_rank is not None:
+        result["per_rank"] = per_rank
     del flush_buf
 
     if args.copy_probe:
@@ -533,6 +815,10 @@ def main():
         result["copy_ceiling"] = probe
         del a, b
 
+    if args.floor_probe:
+        result["flatten_floor"] = flatten_floor(B, u, N, params, stream, dev, gen)
+    if args.contention_probe:
+        result["contention"] = contention_probe(B, u, N, contrib_rows, pre, post, grad, stream, dev)
     if args.floor_probe:
         fb = torch.zeros(1 << 28, device=dev)
         fs = torch.zeros((), device=dev)
@@ -565,8 +851,12 @@ def main():
             "adam_p": adam_p.cpu().numpy(),
             "adam_g": grad.cpu().numpy(),
         }
-        result["cpu_baseline"] = cpu_baseline(host, unit, N, k, S, valid, pre, post, hp,
-                                              rows=layout == B.FSDP_ROWS)
+        one = cpu_baseline(host, unit, N, k, S, valid, pre, post, hp, rows=layout == B.FSDP_ROWS)
+        print("cpu baseline: one core done", file=sys.stderr, flush=True)
+        allc = cpu_baseline_all_cores(host, unit, N, k, S, valid, pre, post, hp,
+                                      rows=layout == B.FSDP_ROWS, threads=host_threads())
+        allc["single_core"] = one
+        result["cpu_baseline"] = allc
     print(json.dumps(result), flush=True)
     return 0
 

@@ -58,7 +58,7 @@ extern "C" {
 #define FSDP_API
 #endif
 
-#define FSDP_ABI_VERSION 2
+#define FSDP_ABI_VERSION 3
 #define FSDP_ALL_RANKS (-1)
 #define FSDP_MAX_NDIM 8
 
@@ -123,15 +123,35 @@ typedef struct {
     int64_t step;          /* t >= 1: the step being taken (1 for the first)   */
 } fsdp_adamw_cfg;
 
+/* Which kernel fsdp_grad_reduce_shard_ex runs (fsdp_reduce_opts.kernel). */
+typedef enum {
+    /* The library's choice: the row-major sweep when a launch holds 32 or more ranks and
+     * the shard 12,288 or more whole 512-output tiles (about 6.3 M outputs), else the
+     * tile kernel.  The sweep sizes its grid to be resident on an otherwise idle device;
+     * when kernels on other streams hold compute units, its waves that do not fit start
+     * only as others finish. */
+    FSDP_REDUCE_AUTO = 0,
+    /* The tile kernel: one 512-output tile per 64-thread workgroup, many short
+     * workgroups, which fill whatever compute units are free. */
+    FSDP_REDUCE_TILES = 1,
+    /* The row-major sweep wherever its loads apply (every contribution 4-byte aligned,
+     * grad_shard and workspace 16-byte aligned, at least one sweep wave of whole tiles);
+     * the tile kernel otherwise. */
+    FSDP_REDUCE_SWEEP = 2
+} fsdp_reduce_kernel;
+
 /* Options of fsdp_grad_reduce_shard_ex. */
 typedef struct {
     float pre_divide;      /* finite, non-zero: divides every term before it is added     */
     float post_divide;     /* finite, non-zero: divides the total                         */
     int32_t group;         /* ranks per sharding group (hybrid sharding).  0, 1 or N: one
-                              flat sequential sum.  Otherwise it must divide N and be at
-                              most 128                                                    */
-    int32_t accumulate;    /* non-zero: add the result to what grad_shard already holds
-                              (N <= 128)                                                  */
+                              flat sequential sum; otherwise it must divide N             */
+    int32_t accumulate;    /* non-zero: add the result to what grad_shard already holds   */
+    int32_t kernel;        /* an fsdp_reduce_kernel (0: FSDP_REDUCE_AUTO)                 */
+    int32_t reserved;      /* ignored; set it to 0                                        */
+    float* workspace;      /* device pointer, 16-byte aligned: fp32 scratch of at least
+                              fsdp_grad_reduce_workspace floats, or NULL when that is 0  */
+    int64_t workspace_len; /* floats the workspace holds                                  */
 } fsdp_reduce_opts;
 
 /* Version of this header the library was built from (FSDP_ABI_VERSION). */
@@ -312,7 +332,7 @@ FSDP_API fsdp_status fsdp_flatten_shard_bf16(const fsdp_unit* unit, const uint16
                                              int32_t k, uint16_t* shard, void* stream);
 
 /*
- * fsdp_grad_reduce_shard with hybrid sharding and accumulation.
+ * fsdp_grad_reduce_shard with hybrid sharding, accumulation and a choice of kernel.
  * Hybrid sharding ([P1] section 3.4, "Sharding Strategies": a ReduceScatter
  * inside each sharding group, then an AllReduce across the replication
  * groups; the sum over all ranks equals the sum of the group sums): the N
@@ -321,13 +341,32 @@ FSDP_API fsdp_status fsdp_flatten_shard_bf16(const fsdp_unit* unit, const uint16
  * Accumulation with communication ([P1] section 3.4, "Communication
  * Optimizations: Overlapping, Prefetching, and Accumulation", "Gradient
  * Accumulation Variants"): out = out + result.
- * Errors as fsdp_grad_reduce_shard, plus FSDP_E_ARG (opts NULL), FSDP_E_RANGE
- * (group does not divide N) and FSDP_E_UNSUPPORTED (group > 128 with
- * group < N, or accumulate with N > 128).
+ * Any N and group: one kernel launch holds up to 128 ranks, and the sums a
+ * longer reduction carries from one launch to the next are stored exactly
+ * (results do not depend on the split).  The output carries them, except
+ * when it must keep its old value (accumulate) or a group is longer than one
+ * launch: then they go to the caller's workspace (see
+ * fsdp_grad_reduce_workspace; calls that share a workspace on one stream run
+ * in order, on different streams they must not share one).
+ * Errors as fsdp_grad_reduce_shard, plus FSDP_E_ARG (opts NULL; workspace NULL
+ * when one is needed), FSDP_E_RANGE (group does not divide N; kernel not an
+ * fsdp_reduce_kernel; workspace_len below what is needed) and FSDP_E_ALIGN
+ * (workspace not 16-byte aligned when one is needed).
  */
 FSDP_API fsdp_status fsdp_grad_reduce_shard_ex(const fsdp_unit* unit, const uint16_t* const* contribs,
                                                const fsdp_reduce_opts* opts, float* grad_shard,
                                                void* stream);
+
+/*
+ * Floats of workspace fsdp_grad_reduce_shard_ex needs for these options (its
+ * group and accumulate; the other fields are not read): 0 when N <= 128, or
+ * when neither accumulating nor hybrid with groups of more than 128 ranks;
+ * else one or two slots of S rounded up to 64 floats (two when accumulating
+ * with groups of more than 128 ranks).  Host only.
+ * Errors: FSDP_E_ARG (NULL unit, opts or n_floats), FSDP_E_RANGE (group).
+ */
+FSDP_API fsdp_status fsdp_grad_reduce_workspace(const fsdp_unit* unit, const fsdp_reduce_opts* opts,
+                                                int64_t* n_floats);
 
 /*
  * Gradient accumulation without communication ([P1] section 3.4, "Gradient

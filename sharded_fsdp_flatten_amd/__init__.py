@@ -7,6 +7,9 @@ with ctypes under the same names (``binding.py``).
 from .binding import (  # noqa: F401
     FSDP_ALL_RANKS,
     FSDP_FLAT,
+    FSDP_REDUCE_AUTO,
+    FSDP_REDUCE_SWEEP,
+    FSDP_REDUCE_TILES,
     FSDP_ROWS,
     FsdpError,
     Unit,
@@ -18,6 +21,7 @@ from .binding import (  # noqa: F401
     fsdp_grad_accumulate,
     fsdp_grad_reduce_shard,
     fsdp_grad_reduce_shard_ex,
+    fsdp_grad_reduce_workspace,
     fsdp_grad_sqnorm,
     fsdp_grad_sqnorm_workspace,
     fsdp_grad_unscale,

@@ -16,7 +16,7 @@ FSDP_FLAT = 1
 FSDP_ROWS = 2
 FSDP_ALL_RANKS = -1
 FSDP_MAX_NDIM = 8
-ABI_VERSION = 2  # FSDP_ABI_VERSION of include/fsdp_flatten.h this binding marshals for
+ABI_VERSION = 3  # FSDP_ABI_VERSION of include/fsdp_flatten.h this binding marshals for
 
 STATUS_NAMES = {0: "FSDP_OK", 1: "FSDP_E_ARG", 2: "FSDP_E_RANGE", 3: "FSDP_E_ALIGN",
                 4: "FSDP_E_OVERFLOW", 5: "FSDP_E_NOMEM", 6: "FSDP_E_HIP",
@@ -52,7 +52,16 @@ class fsdp_adamw_cfg(ctypes.Structure):
 
 class fsdp_reduce_opts(ctypes.Structure):
     _fields_ = [("pre_divide", ctypes.c_float), ("post_divide", ctypes.c_float),
-                ("group", ctypes.c_int32), ("accumulate", ctypes.c_int32)]
+                ("group", ctypes.c_int32), ("accumulate", ctypes.c_int32),
+                ("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace", ctypes.c_void_p), ("workspace_len", ctypes.c_int64)]
+
+
+# fsdp_reduce_kernel
+FSDP_REDUCE_AUTO = 0
+FSDP_REDUCE_TILES = 1
+FSDP_REDUCE_SWEEP = 2
+_REDUCE_KERNELS = {"auto": FSDP_REDUCE_AUTO, "tiles": FSDP_REDUCE_TILES, "sweep": FSDP_REDUCE_SWEEP}
 
 
 _lib = None
@@ -106,6 +115,9 @@ def load() -> ctypes.CDLL:
     lib.fsdp_flatten_shard_bf16.restype = st
     lib.fsdp_grad_reduce_shard_ex.argtypes = [_vp, _vp, ctypes.POINTER(fsdp_reduce_opts), _vp, _vp]
     lib.fsdp_grad_reduce_shard_ex.restype = st
+    lib.fsdp_grad_reduce_workspace.argtypes = [_vp, ctypes.POINTER(fsdp_reduce_opts),
+                                               ctypes.POINTER(ctypes.c_int64)]
+    lib.fsdp_grad_reduce_workspace.restype = st
     lib.fsdp_grad_accumulate.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int32, _vp]
     lib.fsdp_grad_accumulate.restype = st
     lib.fsdp_grad_unscale.argtypes = [_vp, ctypes.c_int32, _vp, ctypes.c_float, _vp, _vp]
@@ -359,18 +371,37 @@ def fsdp_flatten_shard_bf16(unit: Unit, params: Sequence, k: int, shard, stream=
                                           _stream(stream, shard, *params)))
 
 
+def _reduce_opts(pre_divide, post_divide, group, accumulate, kernel, workspace=None):
+    if kernel not in _REDUCE_KERNELS:
+        raise ValueError("kernel must be one of %s" % ", ".join(_REDUCE_KERNELS))
+    ws_len = workspace.numel() if _is_tensor(workspace) else 0
+    return fsdp_reduce_opts(float(pre_divide), float(post_divide), int(group),
+                            1 if accumulate else 0, _REDUCE_KERNELS[kernel], 0,
+                            _addr(workspace, _F32) or None, ws_len)
+
+
+def fsdp_grad_reduce_workspace(unit: Unit, *, group: int = 0, accumulate: bool = False) -> int:
+    """fp32 elements of workspace fsdp_grad_reduce_shard_ex needs for these options (0: none)."""
+    n = ctypes.c_int64()
+    opts = _reduce_opts(1.0, 1.0, group, accumulate, "auto")
+    _check(load().fsdp_grad_reduce_workspace(unit.handle, ctypes.byref(opts), ctypes.byref(n)))
+    return int(n.value)
+
+
 def fsdp_grad_reduce_shard_ex(unit: Unit, contribs: Sequence, pre_divide: float,
                               post_divide: float, grad_shard, *, group: int = 0,
-                              accumulate: bool = False, stream=None) -> None:
-    """Reduction in hybrid groups of `group` ranks, optionally accumulating into grad_shard."""
+                              accumulate: bool = False, kernel: str = "auto", workspace=None,
+                              stream=None) -> None:
+    """Reduction in hybrid groups of `group` ranks, optionally accumulating into grad_shard;
+    `kernel` is "auto", "tiles" or "sweep"; `workspace` is an fp32 tensor of at least
+    fsdp_grad_reduce_workspace(...) elements, or None when that is 0."""
     if len(contribs) != unit.N:
         raise ValueError("need exactly N = %d contributions, got %d" % (unit.N, len(contribs)))
     for r, c in enumerate(contribs):
         _need(c, unit.S, "contribs[%d]" % r)
     _need(grad_shard, unit.S, "grad_shard")
     table = _ptr_table(contribs, _BF16)
-    opts = fsdp_reduce_opts(float(pre_divide), float(post_divide), int(group),
-                            1 if accumulate else 0)
+    opts = _reduce_opts(pre_divide, post_divide, group, accumulate, kernel, workspace)
     _check(load().fsdp_grad_reduce_shard_ex(unit.handle, ctypes.cast(table, _vp),
                                             ctypes.byref(opts), _addr(grad_shard, _F32) or None,
                                             _stream(stream, grad_shard, *contribs)))
@@ -423,5 +454,6 @@ ABI_FUNCTIONS = ["fsdp_abi_version", "fsdp_last_error", "fsdp_status_string", "f
                  "fsdp_unit_destroy", "fsdp_unit_info", "fsdp_unit_param_offset", "fsdp_unit_recv_pitch",
                  "fsdp_flatten_shard", "fsdp_unflatten_copyout", "fsdp_grad_reduce_shard",
                  "fsdp_adam_shard", "fsdp_cast_to_bf16", "fsdp_unflatten_copyout_bf16",
-                 "fsdp_flatten_shard_bf16", "fsdp_grad_reduce_shard_ex", "fsdp_grad_accumulate",
+                 "fsdp_flatten_shard_bf16", "fsdp_grad_reduce_shard_ex", "fsdp_grad_reduce_workspace",
+                 "fsdp_grad_accumulate",
                  "fsdp_grad_unscale", "fsdp_grad_sqnorm_workspace", "fsdp_grad_sqnorm"]

@@ -1,4 +1,6 @@
-"""Build libfsdpflat.so (the C-ABI library) in-tree with hipcc for gfx950.
+"""Build libfsdpflat.so (the C-ABI library) in-tree with hipcc for gfx950, and
+libfsdpprobe.so (hardware floor probes the benchmark times beside the library;
+not part of the data path).
 
     python -m sharded_fsdp_flatten_amd.build
 
@@ -24,6 +26,8 @@ LIB_NAME = "libfsdpflat.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
 
 SOURCES = ["kernels.hip", "plan.cpp", "fsdp_abi.cpp"]
+PROBE_LIB_PATH = os.path.join(HERE, "libfsdpprobe.so")
+PROBE_SOURCES = ["probes.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -42,17 +46,22 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+def _link(sources, path, verbose):
+    tmp = path + ".tmp%d" % os.getpid()
     cmd = [HIPCC, *FLAGS, "-I", INCLUDE, "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", tmp]
+           *[os.path.join(CSRC, s) for s in sources], "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     proc = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if proc.returncode != 0:
         sys.stderr.write(proc.stdout)
-        raise RuntimeError("hipcc failed to build %s" % LIB_NAME)
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError("hipcc failed to build %s" % os.path.basename(path))
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    _link(SOURCES, LIB_PATH, verbose)
+    _link(PROBE_SOURCES, PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

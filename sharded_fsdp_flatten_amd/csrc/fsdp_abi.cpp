@@ -96,7 +96,15 @@ fsdp_status check_buf(const void* p, int64_t count, size_t elem, const char* nam
     return FSDP_OK;
 }
 
-constexpr int64_t kMaxRanksPerLaunch = 128;  // contribution pointers one kernel launch holds
+// The group of a reduction's options, checked: 0 and N are one flat sum (returned as N).
+fsdp_status reduce_group(const fsdp::UnitPlan& u, const fsdp_reduce_opts* opts, int64_t* group) {
+    int64_t g = opts->group;
+    if (g < 0 || g > u.N) return fail(FSDP_E_RANGE, "group must be in [0, N]");
+    if (g == 0) g = u.N;
+    if (u.N % g != 0) return fail(FSDP_E_RANGE, "group must divide N");
+    *group = g;
+    return FSDP_OK;
+}
 
 fsdp_status reduce_impl(const fsdp_unit* unit, const uint16_t* const* contribs,
                         const fsdp_reduce_opts* opts, float* grad_shard, void* stream,
@@ -109,24 +117,31 @@ fsdp_status reduce_impl(const fsdp_unit* unit, const uint16_t* const* contribs,
         return fail(FSDP_E_RANGE, "pre_divide must be finite and non-zero");
     if (!std::isfinite(post) || post == 0.0f)
         return fail(FSDP_E_RANGE, "post_divide must be finite and non-zero");
-    int64_t group = opts->group;
-    if (group < 0 || group > u.N) return fail(FSDP_E_RANGE, "group must be in [0, N]");
-    if (group == 0) group = u.N;
-    if (u.N % group != 0) return fail(FSDP_E_RANGE, "group must divide N");
-    if (group > 1 && group < u.N && group > kMaxRanksPerLaunch)
-        return fail(FSDP_E_UNSUPPORTED, "hybrid groups of more than 128 ranks");
-    if (opts->accumulate && u.N > kMaxRanksPerLaunch)
-        return fail(FSDP_E_UNSUPPORTED, "accumulation over more than 128 ranks");
+    int64_t group = 0;
     fsdp_status s;
+    if ((s = reduce_group(u, opts, &group)) != FSDP_OK) return s;
+    if (opts->kernel != FSDP_REDUCE_AUTO && opts->kernel != FSDP_REDUCE_TILES &&
+        opts->kernel != FSDP_REDUCE_SWEEP)
+        return fail(FSDP_E_RANGE, "kernel must be FSDP_REDUCE_AUTO, _TILES or _SWEEP");
     if ((s = check_ptr_table(reinterpret_cast<const void* const*>(contribs),
                              static_cast<size_t>(u.N), nullptr, u.S, sizeof(uint16_t),
                              "contribs")) != FSDP_OK)
         return s;
     if ((s = check_buf(grad_shard, u.S, sizeof(float), "grad_shard")) != FSDP_OK) return s;
+    const int64_t need = fsdp::reduce_workspace_floats(u.N, u.S, group, opts->accumulate != 0);
+    float* ws = need > 0 ? opts->workspace : nullptr;
+    if (need > 0) {
+        if (!ws) return fail(FSDP_E_ARG, "these options need a workspace of " +
+                                             std::to_string(need) + " floats; workspace is NULL");
+        if (!aligned_to(ws, 16)) return fail(FSDP_E_ALIGN, "workspace is not 16-byte aligned");
+        if (opts->workspace_len < need)
+            return fail(FSDP_E_RANGE, "workspace holds " + std::to_string(opts->workspace_len) +
+                                          " floats; these options need " + std::to_string(need));
+    }
     if (u.S == 0) return ok();
-    const hipError_t e =
-        fsdp::launch_grad_reduce(contribs, u.N, u.S, pre, post, group, opts->accumulate != 0,
-                                 grad_shard, static_cast<hipStream_t>(stream));
+    const hipError_t e = fsdp::launch_grad_reduce(
+        contribs, u.N, u.S, pre, post, group, opts->accumulate != 0, grad_shard, ws,
+        static_cast<fsdp::ReduceKernel>(opts->kernel), static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, (std::string(who) + " launch").c_str());
     return ok();
 }
@@ -280,7 +295,9 @@ fsdp_status fsdp_grad_reduce_shard(const fsdp_unit* unit, const uint16_t* const*
                                    float pre_divide, float post_divide, float* grad_shard,
                                    void* stream) {
     return guarded("fsdp_grad_reduce_shard", [&]() -> fsdp_status {
-        const fsdp_reduce_opts opts{pre_divide, post_divide, 0, 0};
+        fsdp_reduce_opts opts{};
+        opts.pre_divide = pre_divide;
+        opts.post_divide = post_divide;
         return reduce_impl(unit, contribs, &opts, grad_shard, stream, "fsdp_grad_reduce_shard");
     });
 }
@@ -290,6 +307,20 @@ fsdp_status fsdp_grad_reduce_shard_ex(const fsdp_unit* unit, const uint16_t* con
                                       void* stream) {
     return guarded("fsdp_grad_reduce_shard_ex", [&]() -> fsdp_status {
         return reduce_impl(unit, contribs, opts, grad_shard, stream, "fsdp_grad_reduce_shard_ex");
+    });
+}
+
+fsdp_status fsdp_grad_reduce_workspace(const fsdp_unit* unit, const fsdp_reduce_opts* opts,
+                                       int64_t* n_floats) {
+    return guarded("fsdp_grad_reduce_workspace", [&]() -> fsdp_status {
+        if (!unit || !opts || !n_floats)
+            return fail(FSDP_E_ARG, "unit, opts and n_floats must not be NULL");
+        const fsdp::UnitPlan& u = unit->plan;
+        int64_t group = 0;
+        const fsdp_status s = reduce_group(u, opts, &group);
+        if (s != FSDP_OK) return s;
+        *n_floats = fsdp::reduce_workspace_floats(u.N, u.S, group, opts->accumulate != 0);
+        return ok();
     });
 }
 

@@ -17,13 +17,24 @@ enum class Pipe { kF32toF32, kF32toBF16, kBF16toBF16 };
 // launches if the table is larger than one kernel argument block holds.
 hipError_t launch_segcopy(const std::vector<CopySeg>& segs, Pipe pipe, hipStream_t stream);
 
+// Which reduction kernel runs: the default choice (the row-major sweep for many ranks and
+// long outputs, else the tile kernel), the tile kernel only, or the sweep wherever its loads
+// apply (every contribution 4-byte aligned, the output and workspace 16-byte aligned, at
+// least one sweep wave of whole tiles).
+enum class ReduceKernel { kAuto = 0, kTiles = 1, kSweep = 2 };
+
+// Floats of workspace launch_grad_reduce needs (0: none): the sums it carries between
+// launches when the ranks do not fit one launch and the output cannot carry them.
+int64_t reduce_workspace_floats(int64_t n_contrib, int64_t len, int64_t group, bool accumulate);
+
 // fp32 reduction of `n_contrib` bf16 contributions of `len` elements each:
-// in groups of `group` consecutive ranks (group == n_contrib: one flat sum),
+// in groups of `group` consecutive ranks (group <= 1 or >= n_contrib: one flat sum),
 // divided by pre (each term) and post (the total); with `accumulate` the
-// result is added to what `out` holds.
+// result is added to what `out` holds.  `workspace` holds reduce_workspace_floats
+// floats (16-byte aligned), or is unused when that is 0.
 hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib, int64_t len,
                               float pre, float post, int64_t group, bool accumulate, float* out,
-                              hipStream_t stream);
+                              float* workspace, ReduceKernel kernel, hipStream_t stream);
 
 // acc = (init ? 0 : acc) + fp32(grad), elementwise over len.
 hipError_t launch_grad_accumulate(const uint16_t* grad, float* acc, int64_t len, bool init,

@@ -19,7 +19,8 @@
 //     the bf16 copies.  The host planner turns the layout into a short table of
 //     (src, dst, length[, block stride]) segments passed in the kernel argument
 //     block; each workgroup takes one tile of one segment (the tile -> segment
-//     lookup is a wave-uniform binary search on scalar registers), so no lane
+//     lookup is wave-uniform, on scalar registers: a count over tables of up to 4
+//     segments, loaded at once, a binary search over larger ones), so no lane
 //     ever searches and every tile is a straight streaming copy.  Launches of
 //     2^18 tiles or more hand each XCD runs of 256 consecutive tiles.  When source
 //     and destination are not 16-byte co-aligned, a scalar head aligns the
@@ -31,16 +32,19 @@
 //     whole tiles swap halves across lanes so each store writes 1 KiB; the tile
 //     the output's end cuts runs first, its last len % 8 outputs one per lane.
 //     From 32 ranks and 12,288 whole tiles on, a row-major sweep instead: each
-//     wave holds 16 tiles' sums and walks the ranks in order, the grid sized to be
-//     resident at once (each XCD one contiguous run of waves), so HBM serves a few
-//     contribution rows at a time.
+//     wave holds 16 tiles' sums (8 with hybrid groups, whose sums it also holds)
+//     and walks the ranks in order, the grid sized to be resident at once (each
+//     XCD one contiguous run of waves), so HBM serves a few contribution rows at
+//     a time.  More ranks than one launch holds (128) take several launches that
+//     carry their exact running sums through the output or a caller's workspace.
 //   - adamw: elementwise over 8 elements per lane, 128-bit loads and stores.
 //     Its state is read and written back in place: plain loads measure faster
 //     than nt ones (6.5 vs 5.6 TB/s), and nt stores put its writes in HBM within
 //     its own launch (plain stores leave them dirty in the 256 MB Infinity Cache,
 //     which costs the next kernels, or AdamW itself once they outgrow it).
-//   - accumulate, unscale: elementwise in place, four 16-byte vectors per lane
-//     (a long accumulation hands each XCD runs of 64 blocks).
+//   - accumulate: 16-byte bf16 loads (8 per lane), exchanged across lanes so that
+//     each fp32 load and store instruction covers 1 KiB (a long accumulation hands
+//     each XCD runs of 128 blocks); unscale: in place, four 16-byte vectors per lane.
 //   - sqnorm: per-parameter sums of squares in binary64, one tile per workgroup
 //     into a workspace, then one workgroup per parameter, in fixed orders.
 // Every binary32 step is one IEEE operation, in the order the CPU oracle fixes;
@@ -65,93 +69,47 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 
-// Launch shapes (tuned on MI355X; each can be overridden with -D for tuning builds).
-#ifndef FSDP_COPY_THREADS
-#define FSDP_COPY_THREADS 256
-#endif
-#ifndef FSDP_F32_VPL
-#define FSDP_F32_VPL 1      // 4-element vectors per lane per tile, fp32 output
-#endif
-#ifndef FSDP_BF16_VPL
-#define FSDP_BF16_VPL 2     // 4-element vectors per lane per tile, bf16 output
-#endif
-#ifndef FSDP_B16_VPL
-#define FSDP_B16_VPL 1      // 8-element vectors per lane per tile, bf16 -> bf16
-#endif
-#ifndef FSDP_REDUCE_THREADS
-#define FSDP_REDUCE_THREADS 64
-#endif
-#ifndef FSDP_REDUCE_AHEAD
-#define FSDP_REDUCE_AHEAD 8
-#endif
-#ifndef FSDP_SWEEP_MIN_RANKS
-#define FSDP_SWEEP_MIN_RANKS 32  // the reduction sweeps ranks row-major from this many on
-#endif
-#ifndef FSDP_SWEEP_V
-#define FSDP_SWEEP_V 16          // whole tiles a sweep wave holds (8, 12, 16: 6.23, 6.36, 6.53 TB/s)
-#endif
-#ifndef FSDP_SWEEP_MIN_TILES
-#define FSDP_SWEEP_MIN_TILES 12288  // and from this many whole 512-output tiles on
-#endif
-#ifndef FSDP_TILE_STORE_CPOL
-// Whole-tile stores of the copies: 0 = global nt stores, else the cache-policy operand of
-// buffer stores (2 nt, 16 sc1 = device scope, 18 both).  Device-scope nt stores (18) against
-// global nt stores on the GPT-175B unit (HIP events, alternating processes on one box):
-// copy-out 6.48-6.50 vs 6.44-6.45 TB/s, rank flatten 5.26-5.39 vs 4.87-4.94, bf16 copies
-// 6.65-6.69 vs 6.24-6.30; buffer nt stores (2) matched the global ones, and sc1 alone slowed
-// the next kernel (AdamW) by a third.
-#define FSDP_TILE_STORE_CPOL 18
-#endif
-#ifndef FSDP_XCD_MIN_TILES
+// Launch shapes and access policies, each measured on MI355X (the figures are TB/s on the
+// GPT-175B block unit unless stated; alternating processes on one box).
+constexpr int kThreads = 256;        // copy engine workgroup (also accumulate, unscale)
+constexpr int kF32Vpl = 1;           // 4-element vectors per lane per tile, fp32 output
+constexpr int kBF16Vpl = 2;          // 4-element vectors per lane per tile, fp32 -> bf16
+constexpr int kB16Vpl = 1;           // 8-element vectors per lane per tile, bf16 -> bf16
+// Whole-tile stores of the copies: buffer stores with this cache-policy operand, 18 =
+// sc1 (device scope) + nt.  Against global nt stores: copy-out 6.48-6.50 vs 6.44-6.45,
+// rank flatten 5.26-5.39 vs 4.87-4.94 (HIP events), bf16 copies 6.65-6.69 vs 6.24-6.30;
+// nt alone (2) matched the global ones, and sc1 alone slowed the next kernel (AdamW) by a
+// third.
+constexpr int kTileStoreCpol = 18;
 // From this many tiles (workgroups) on, a copy hands each of the eight XCDs runs of
-// FSDP_XCD_CHUNK consecutive tiles instead of every eighth tile.  GPT-175B copy-out (885k
-// tiles), one box, alternating processes: dispatch order 6.46-6.49 TB/s, one contiguous run
-// per XCD 6.61-6.65, runs of 64 / 128 / 256 / 512 tiles 6.65-6.67 / 6.76 / 6.76-6.78 /
-// 6.62-6.63.  One run per XCD made 64-256 MB copies 3-7% slower; runs of 256 left every
-// size from 8 MB to 1 GB as fast as the dispatch order.
-#define FSDP_XCD_MIN_TILES (1u << 18)
-#endif
-#ifndef FSDP_XCD_CHUNK
-#define FSDP_XCD_CHUNK 256u
-#endif
-#ifndef FSDP_ACC_XCD_CHUNK
-// The in-place local accumulation over all L (442k blocks) takes runs of 64 blocks per XCD:
-// 6.09-6.12 vs 6.01-6.08 TB/s in dispatch order; runs of 16 / 32 / 256 blocks 5.88-5.95 /
-// 5.96-6.01 / 5.99-6.00, one run per XCD 5.94-5.95 (one box, alternating processes).
-#define FSDP_ACC_XCD_CHUNK 64u
-#endif
-#ifndef FSDP_ACC_VPL
-#define FSDP_ACC_VPL 4          // 4-element vectors per lane in the local accumulation (1/2/4: 5.70/5.96/6.07 TB/s)
-#endif
-#ifndef FSDP_UNSCALE_VPL
-#define FSDP_UNSCALE_VPL 4      // 4-element vectors per lane in the gradient unscale
-#endif
-#ifndef FSDP_ACC_NT
-#define FSDP_ACC_NT 1       // local accumulation: nt measured faster (5.9 vs 5.6 TB/s)
-#endif
-#ifndef FSDP_ADAM_THREADS
-#define FSDP_ADAM_THREADS 256
-#endif
-#ifndef FSDP_ADAM_NT_LOAD
-#define FSDP_ADAM_NT_LOAD 0   // AdamW reads p, g, m, v with plain loads
-#endif
-#ifndef FSDP_ADAM_NT_STORE
-#define FSDP_ADAM_NT_STORE 1  // and streams p, m, v back with nt stores
-#endif
-#ifndef FSDP_ADAM_STORE_CPOL
-// AdamW's whole-block stores: 0 = global stores (nt as FSDP_ADAM_NT_STORE says), else buffer
-// stores with this cache-policy operand.  Buffer nt stores (2) measured 6.62-6.65 TB/s against
-// 6.48-6.55 for global nt stores; device-scope nt stores (18) 5.46-5.59.  Those also slowed
-// the in-place accumulation and unscale, which keep global stores.
-#define FSDP_ADAM_STORE_CPOL 2
-#endif
+// kXcdChunk consecutive tiles instead of every eighth tile.  Copy-out (885k tiles):
+// dispatch order 6.46-6.49, one contiguous run per XCD 6.61-6.65, runs of 64 / 128 / 256 /
+// 512 tiles 6.65-6.67 / 6.76 / 6.76-6.78 / 6.62-6.63.  One run per XCD made 64-256 MB
+// copies 3-7% slower; runs of 256 left every size from 8 MB to 1 GB as fast as the
+// dispatch order.
+constexpr uint32_t kXcdMinTiles = 1u << 18;
+constexpr uint32_t kXcdChunk = 256u;
+constexpr int kReduceThreads = 64;   // reduction tile kernel: one wave per 512-output tile
+constexpr int kReduceAhead = 8;      // ranks loaded before their adds in the tile kernel
+constexpr int kSweepMinRanks = 32;   // the flat reduction sweeps ranks row-major from this many
+constexpr int kSweepMinTiles = 12288;  // ... and from this many whole 512-output tiles on
+constexpr int kSweepV = 16;          // whole tiles a flat sweep wave holds (8/12/16: 6.23/6.36/6.53)
+constexpr int kHybridSweepV = 8;     // and a hybrid one (it also holds its group's sums)
+constexpr int kUnscaleVpl = 4;       // 4-element vectors per lane in the gradient unscale
+// The in-place local accumulation over all L of the GPT-175B unit (885k blocks of 2048) takes
+// runs of 128 blocks per XCD: 6.38-6.40 TB/s, against 5.87-5.88 in dispatch order and runs of
+// 16 / 32 / 64 / 256 blocks 5.98-5.99 / 6.12-6.21 / 6.32-6.34 / 6.37-6.38 (HIP events, two
+// rounds in one process).
+constexpr uint32_t kAccXcdChunk = 128u;
+constexpr int kAdamThreads = 256;
+// AdamW reads p, g, m, v with plain loads (nt loads: 5.57 against 6.46) and stores whole
+// blocks with buffer stores of this cache policy, 2 = nt: 6.62-6.65 against 6.48-6.55 for
+// global nt stores; device-scope nt stores (18) 5.46-5.59.
+constexpr int kAdamStoreCpol = 2;
 
-constexpr int kThreads = FSDP_COPY_THREADS;
 constexpr int kMaxSegs = 48;           // segments per launch (kernel-argument budget)
 constexpr int kMaxContrib = 128;       // contribution pointers per reduce launch
-constexpr int kReduceThreads = FSDP_REDUCE_THREADS;
 static_assert(kReduceThreads % 64 == 0, "reduce workgroups are whole wave64s (lane exchange)");
-constexpr int kAdamThreads = FSDP_ADAM_THREADS;
 
 // ---------------------------------------------------------------------------
 // memory helpers: vector global accesses with the non-temporal hint (streamed
@@ -183,16 +141,6 @@ __device__ __forceinline__ void stu4(void* p, u4 v) {
 }
 __device__ __forceinline__ void stu2(void* p, u2 v) {
     __builtin_nontemporal_store(v, reinterpret_cast<u2*>(p));
-}
-template <bool kNT>
-__device__ __forceinline__ f4 ld4s(const float* p) {
-    if constexpr (kNT) return ld4(p);
-    else return *reinterpret_cast<const f4*>(p);
-}
-template <bool kNT>
-__device__ __forceinline__ void st4s(float* p, f4 v) {
-    if constexpr (kNT) st4(p, v);
-    else *reinterpret_cast<f4*>(p) = v;
 }
 
 // fp32 pair -> packed bf16 pair (element 0 in the low half), round to nearest
@@ -233,29 +181,24 @@ __device__ __forceinline__ void bst2(__amdgpu_buffer_rsrc_t r, int off, u2 v) {
 // its first element, which every lane of the workgroup shares.
 template <typename SrcT, typename DstT> struct Cp;
 template <> struct Cp<float, float> {
-    static constexpr int E = 4, kVpl = FSDP_F32_VPL;
+    static constexpr int E = 4, kVpl = kF32Vpl;
     static constexpr unsigned kDstAlign = 16;  // bytes a vector store needs
     using V = f4;
     __device__ static V load(const float* p) { return ld4(p); }
     __device__ static V loadw(const float* p) { return ld4w(p); }
     __device__ static void put(float* d, V x) { st4(d, x); }
     __device__ static void put_tile(float* d, const V* x) {
-#if FSDP_TILE_STORE_CPOL
         const auto r = block_rsrc(d, kThreads * E * kVpl * 4);
 #pragma unroll
         for (int u = 0; u < kVpl; ++u)
-            bst4<FSDP_TILE_STORE_CPOL>(r, 16 * (threadIdx.x + u * kThreads), x[u]);
-#else
-#pragma unroll
-        for (int u = 0; u < kVpl; ++u) put(d + E * (threadIdx.x + u * kThreads), x[u]);
-#endif
+            bst4<kTileStoreCpol>(r, 16 * (threadIdx.x + u * kThreads), x[u]);
     }
     __device__ static void put1(float* d, float x) { *d = x; }
     __device__ static void zero(float* d) { st4(d, f4{0.0f, 0.0f, 0.0f, 0.0f}); }
     __device__ static void zero1(float* d) { *d = 0.0f; }
 };
 template <> struct Cp<float, uint16_t> {
-    static constexpr int E = 4, kVpl = FSDP_BF16_VPL;
+    static constexpr int E = 4, kVpl = kBF16Vpl;
     static constexpr unsigned kDstAlign = 8;
     using V = f4;
     __device__ static V load(const float* p) { return ld4(p); }
@@ -264,23 +207,18 @@ template <> struct Cp<float, uint16_t> {
         stu2(d, u2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])});
     }
     __device__ static void put_tile(uint16_t* d, const V* x) {
-#if FSDP_TILE_STORE_CPOL
         const auto r = block_rsrc(d, kThreads * E * kVpl * 2);
 #pragma unroll
         for (int u = 0; u < kVpl; ++u)
-            bst2<FSDP_TILE_STORE_CPOL>(r, 8 * (threadIdx.x + u * kThreads),
-                                       u2{pack_bf16x2(x[u][0], x[u][1]), pack_bf16x2(x[u][2], x[u][3])});
-#else
-#pragma unroll
-        for (int u = 0; u < kVpl; ++u) put(d + E * (threadIdx.x + u * kThreads), x[u]);
-#endif
+            bst2<kTileStoreCpol>(r, 8 * (threadIdx.x + u * kThreads),
+                                 u2{pack_bf16x2(x[u][0], x[u][1]), pack_bf16x2(x[u][2], x[u][3])});
     }
     __device__ static void put1(uint16_t* d, float x) { *d = to_bf16(x); }
     __device__ static void zero(uint16_t* d) { stu2(d, u2{0u, 0u}); }
     __device__ static void zero1(uint16_t* d) { *d = 0; }
 };
 template <> struct Cp<uint16_t, uint16_t> {
-    static constexpr int E = 8, kVpl = FSDP_B16_VPL;
+    static constexpr int E = 8, kVpl = kB16Vpl;
     static constexpr unsigned kDstAlign = 16;
     using V = u4;
     __device__ static V load(const uint16_t* p) { return ldu4(p); }
@@ -291,16 +229,10 @@ template <> struct Cp<uint16_t, uint16_t> {
     }
     __device__ static void put(uint16_t* d, V x) { stu4(d, x); }
     __device__ static void put_tile(uint16_t* d, const V* x) {
-#if FSDP_TILE_STORE_CPOL
         const auto r = block_rsrc(d, kThreads * E * kVpl * 2);
 #pragma unroll
         for (int u = 0; u < kVpl; ++u)
-            bst4<FSDP_TILE_STORE_CPOL>(r, 16 * (threadIdx.x + u * kThreads),
-                                       __builtin_bit_cast(f4, x[u]));
-#else
-#pragma unroll
-        for (int u = 0; u < kVpl; ++u) put(d + E * (threadIdx.x + u * kThreads), x[u]);
-#endif
+            bst4<kTileStoreCpol>(r, 16 * (threadIdx.x + u * kThreads), __builtin_bit_cast(f4, x[u]));
     }
     __device__ static void put1(uint16_t* d, uint16_t x) { *d = x; }
     __device__ static void zero(uint16_t* d) { stu4(d, u4{0u, 0u, 0u, 0u}); }
@@ -312,20 +244,25 @@ constexpr int tile_elems() { return kThreads * Cp<SrcT, DstT>::E * Cp<SrcT, DstT
 // ---------------------------------------------------------------------------
 // segcopy
 // ---------------------------------------------------------------------------
+// One segment of a launch; the fields a single-segment launch reads come first.
 struct DevSeg {
     const void* src;  // nullptr: zero fill
     void* dst;
-    int64_t blk_n, last_n, src_stride, dst_stride;
+    int64_t blk_n, last_n;
     uint32_t nblk, tiles_per_blk, tile0, unused;
+    int64_t src_stride, dst_stride;
 };
+// A launch's segments, passed by value in the kernel-argument block: a table of kCap entries,
+// the smallest of 1, 4, 16 and kMaxSegs that holds the launch's segments.
+template <int kCap>
 struct SegTable {
     uint32_t ntiles;
     uint32_t nseg;
     uint32_t xcd_runs;  // tiles in XCD-chunked order (xcd_chunked)
     uint32_t unused;
-    DevSeg seg[kMaxSegs];
+    DevSeg seg[kCap];
 };
-static_assert(sizeof(SegTable) <= 4096, "segment table must fit one kernel argument block");
+static_assert(sizeof(SegTable<kMaxSegs>) <= 4096, "segment table must fit one kernel argument block");
 
 // The dispatcher deals a launch's workgroups to MI355X's eight XCDs in turn (workgroup b to
 // XCD b % 8).  This maps b to the tile it runs so that each XCD takes one contiguous run of
@@ -428,21 +365,10 @@ __device__ __forceinline__ void tile_general(const SrcT* s, DstT* d, int n, SrcT
     }
 }
 
-// One tile per workgroup (grid = number of tiles).
+// Tile `local` of segment sg (tiles count from the segment's first).
 template <typename SrcT, typename DstT, bool kGeneral>
-__global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable t) {
+__device__ __forceinline__ void copy_tile(const DevSeg& sg, uint32_t local, SrcT* lds) {
     constexpr int kTile = tile_elems<SrcT, DstT>();
-    __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral && sizeof(SrcT) == 2 ? kTile + 16 : 8];
-    const uint32_t tile =
-        t.xcd_runs ? xcd_chunked<FSDP_XCD_CHUNK>(blockIdx.x, t.ntiles) : blockIdx.x;
-    // wave-uniform lookup of the segment holding this tile
-    uint32_t lo = 0, hi = t.nseg - 1;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) >> 1;
-        if (t.seg[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
-    }
-    const DevSeg& sg = t.seg[lo];
-    const uint32_t local = tile - sg.tile0;
     const uint32_t b = sg.nblk == 1 ? 0u : local / sg.tiles_per_blk;
     const uint32_t tb = local - b * sg.tiles_per_blk;
     const int64_t e0 = static_cast<int64_t>(tb) * kTile;
@@ -461,19 +387,74 @@ __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable t) {
         tile_aligned<SrcT, DstT>(s, d, n);
 }
 
+// One tile per workgroup (grid = number of tiles).  The tile's segment is found from the
+// table with wave-uniform scalar loads, and a workgroup's first vector load waits for them.
+// Tables of up to 4 segments are read at the start with one wait -- the empty asm statements
+// pin the loads there, where the compiler would issue each just before its first use, after
+// the previous one's wait -- and the segment is found by counting first tiles; one-segment
+// tables load the segment's fields with them.  On the GPT-175B block's rank flatten (rocprofv3,
+// cold cache, two rounds on one box) a one-segment shard took 18.72-18.84 against 19.04-19.28
+// us with the search, a two-segment one 19.24-19.28 against 19.64-19.76.  Larger tables
+// search: counting 16 entries made the five-segment rank 0 take 21.0-21.5 us against 20.2-20.3.
+template <typename SrcT, typename DstT, bool kGeneral, int kCap>
+__global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable<kCap> t) {
+    constexpr int kTile = tile_elems<SrcT, DstT>();
+    __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral && sizeof(SrcT) == 2 ? kTile + 16 : 8];
+    const uint32_t ntiles = t.ntiles, nseg = t.nseg, xcdr = t.xcd_runs;
+    uint32_t lo = 0;
+    if constexpr (kCap <= 4) {
+        uint32_t t0[kCap];
+#pragma unroll
+        for (int i = 0; i < kCap; ++i) t0[i] = t.seg[i].tile0;
+        asm volatile("" ::"s"(ntiles), "s"(nseg), "s"(xcdr));
+#pragma unroll
+        for (int i = 0; i < kCap; ++i) asm volatile("" ::"s"(t0[i]));
+        if constexpr (kCap == 1) {
+            const DevSeg& z = t.seg[0];
+            asm volatile("" ::"s"(z.src), "s"(z.dst), "s"(z.blk_n), "s"(z.last_n), "s"(z.nblk),
+                         "s"(z.tiles_per_blk), "s"(z.src_stride), "s"(z.dst_stride));
+        }
+        const uint32_t tile = xcdr ? xcd_chunked<kXcdChunk>(blockIdx.x, ntiles) : blockIdx.x;
+#pragma unroll
+        for (int i = 1; i < kCap; ++i) lo += (static_cast<uint32_t>(i) < nseg && t0[i] <= tile) ? 1u : 0u;
+        const DevSeg& sg = t.seg[lo];
+        copy_tile<SrcT, DstT, kGeneral>(sg, tile - sg.tile0, lds);
+    } else {
+        const uint32_t tile = xcdr ? xcd_chunked<kXcdChunk>(blockIdx.x, ntiles) : blockIdx.x;
+        uint32_t hi = nseg - 1;
+        while (lo < hi) {
+            const uint32_t mid = (lo + hi + 1) >> 1;
+            if (t.seg[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
+        }
+        const DevSeg& sg = t.seg[lo];
+        copy_tile<SrcT, DstT, kGeneral>(sg, tile - sg.tile0, lds);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // gradient reduction
 // ---------------------------------------------------------------------------
 enum PreMode { kPreNone = 0, kPreRecip = 1, kPreDiv = 2 };
 
+// A reduction over more ranks than one launch's pointer table holds takes several
+// launches in rank order (plan_reduce); between them the running sums sit in HBM, stored
+// exactly: the total (the flat sum, or the sum of the completed groups) in `carry_t`, and,
+// when a group is longer than one launch, that group's partial sum in `carry_s`.  The
+// flags say what a launch loads and stores; per output the operations and their order
+// are those of one launch over all ranks.
+constexpr uint32_t kTIn = kReduceTIn, kSIn = kReduceSIn, kTOut = kReduceTOut,
+                   kSOut = kReduceSOut, kLast = kReduceLast;
+
 struct ReduceArgs {
     const uint16_t* c[kMaxContrib];
     float* out;
+    float* carry_t;
+    float* carry_s;
     int64_t len;
-    int32_t nc;          // contributions in this launch
-    int32_t group;       // hybrid: ranks per group (the launch holds whole groups)
-    int32_t first;       // the sum starts in this launch (else out holds the partial)
-    int32_t last;        // this launch divides by post (and accumulates)
+    int32_t nc;      // contributions in this launch
+    int32_t group;   // hybrid: ranks per group
+    int32_t pos0;    // hybrid: position of this launch's first rank in its group
+    uint32_t flags;
     float pre, rpre, post;
 };
 
@@ -570,13 +551,12 @@ __device__ __forceinline__ void load_out8(float* v, const float* out) {
 template <int kPre, int kLd>
 __device__ __forceinline__ void add_ranks(float* acc, int r, int end, int64_t j0,
                                           const ReduceArgs& a) {
-    constexpr int kAhead = FSDP_REDUCE_AHEAD;
-    for (; r + kAhead <= end; r += kAhead) {
-        Raw x[kAhead];
+    for (; r + kReduceAhead <= end; r += kReduceAhead) {
+        Raw x[kReduceAhead];
 #pragma unroll
-        for (int u = 0; u < kAhead; ++u) x[u] = load_raw<kLd>(a, r + u, j0);
+        for (int u = 0; u < kReduceAhead; ++u) x[u] = load_raw<kLd>(a, r + u, j0);
 #pragma unroll
-        for (int u = 0; u < kAhead; ++u) add8<kPre>(acc, finish<kLd>(x[u], a, r + u), a);
+        for (int u = 0; u < kReduceAhead; ++u) add8<kPre>(acc, finish<kLd>(x[u], a, r + u), a);
     }
     for (; r < end; ++r) add8<kPre>(acc, finish<kLd>(load_raw<kLd>(a, r, j0), a, r), a);
 }
@@ -586,10 +566,10 @@ __device__ __forceinline__ void add_ranks(float* acc, int r, int end, int64_t j0
 template <int kPre, bool kHybrid, bool kAccum>
 __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
     constexpr int kBatch = 8;
-    bool have = !a.first;
-    float acc = have ? a.out[j] : 0.0f;
-    float s = 0.0f;
-    int pos = 0;
+    bool have = (a.flags & kTIn) != 0;
+    float acc = have ? a.carry_t[j] : 0.0f;
+    float s = (kHybrid && (a.flags & kSIn)) ? a.carry_s[j] : 0.0f;
+    int pos = a.pos0;
     for (int r = 0; r < a.nc; r += kBatch) {
         const int cnt = min(kBatch, a.nc - r);
         float t[kBatch];
@@ -600,7 +580,7 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
         for (int u = 0; u < kBatch; ++u) {
             if (u >= cnt) break;
             if constexpr (!kHybrid) {
-                // one running sum in rank order, continuing the previous launch's
+                // one running sum in rank order
                 acc = have ? acc + t[u] : t[u];
                 have = true;
             } else {
@@ -614,11 +594,14 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
             }
         }
     }
-    if (a.last) {
+    if (a.flags & kLast) {
         acc = acc / a.post;
         if constexpr (kAccum) acc = a.out[j] + acc;
+        a.out[j] = acc;
+        return;
     }
-    a.out[j] = acc;
+    if (a.flags & kTOut) a.carry_t[j] = acc;
+    if (kHybrid && (a.flags & kSOut)) a.carry_s[j] = s;
 }
 
 // Stores a wave's 512 outputs of one whole tile, lane l holding outputs 8l .. 8l+7
@@ -641,72 +624,100 @@ __device__ __forceinline__ void store_whole8(float* wave_out, const float* acc) 
     }
 }
 
+// A lane's 8 outputs j0 .. j0+7 into `base` (an array indexed like the output).
+// kWhole: the wave's whole tile at once (every lane of the wave takes part).
+template <bool kWhole>
+__device__ __forceinline__ void store8(float* base, int64_t j0, const float* v) {
+    if constexpr (kWhole) {
+        store_whole8(base + (j0 - 8 * static_cast<int64_t>(threadIdx.x & 63)), v);
+    } else {
+        st4(base + j0, f4{v[0], v[1], v[2], v[3]});
+        st4(base + j0 + 4, f4{v[4], v[5], v[6], v[7]});
+    }
+}
+
+// End of a launch for a lane's 8 outputs: the last launch divides the total by post,
+// adds it to what `out` holds when accumulating, and stores it; an earlier launch
+// stores what the next one carries on with.
+template <bool kAccum, bool kWhole, bool kHybrid>
+__device__ __forceinline__ void finish8(const ReduceArgs& a, int64_t j0, float* acc, const float* s) {
+    if (a.flags & kLast) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = acc[e] / a.post;
+        if constexpr (kAccum) {
+            float prev[8];
+            load_out8(prev, a.out + j0);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] = prev[e] + acc[e];
+        }
+        store8<kWhole>(a.out, j0, acc);
+        return;
+    }
+    if (a.flags & kTOut) store8<kWhole>(a.carry_t, j0, acc);
+    if (kHybrid && (a.flags & kSOut)) store8<kWhole>(a.carry_s, j0, s);
+}
+
 // The 8 outputs j0 .. j0+7 of one lane over this launch's ranks.  kWhole: the tile
 // is whole and is stored with store_whole8; otherwise each lane stores its own 8.
 template <int kPre, int kLd, bool kHybrid, bool kAccum, bool kWhole>
 __device__ __forceinline__ void reduce_lane(const ReduceArgs& a, int64_t j0) {
-    constexpr int kEpt = 8;
-    constexpr int kAhead = FSDP_REDUCE_AHEAD;
-    float acc[kEpt];
+    float acc[8];
     if constexpr (!kHybrid) {
         int r = 0;
-        if (a.first) {
+        if (a.flags & kTIn) {
+            load_out8(acc, a.carry_t + j0);
+        } else {
             set8<kPre>(acc, finish<kLd>(load_raw<kLd>(a, 0, j0), a, 0), a);
             r = 1;
-        } else {
-            load_out8(acc, a.out + j0);
         }
         add_ranks<kPre, kLd>(acc, r, a.nc, j0, a);
+        finish8<kAccum, kWhole, false>(a, j0, acc, acc);
     } else {
-        // Loads run kAhead ranks ahead regardless of group boundaries; a wave-uniform
-        // position-in-group counter starts each group's sum at its first rank and
-        // folds it into the total after its last.
-        bool have = !a.first;
-        if (have) load_out8(acc, a.out + j0);
-        float s[kEpt];
-        int pos = 0;
-        for (int r = 0; r < a.nc; r += kAhead) {
-            const int n = min(kAhead, a.nc - r);
-            Raw x[kAhead];
+        // Loads run kReduceAhead ranks ahead regardless of group boundaries; a
+        // wave-uniform position-in-group counter starts each group's sum at its first
+        // rank and folds it into the total after its last.
+        bool have = (a.flags & kTIn) != 0;
+        if (have) {
+            load_out8(acc, a.carry_t + j0);
+        } else {
 #pragma unroll
-            for (int u = 0; u < kAhead; ++u)
+            for (int e = 0; e < 8; ++e) acc[e] = 0.0f;  // not read before the first fold
+        }
+        float s[8];
+        int pos = a.pos0;
+        if (a.flags & kSIn) {
+            load_out8(s, a.carry_s + j0);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) s[e] = 0.0f;  // pos0 == 0: set by the first rank
+        }
+        for (int r = 0; r < a.nc; r += kReduceAhead) {
+            const int n = min(kReduceAhead, a.nc - r);
+            Raw x[kReduceAhead];
+#pragma unroll
+            for (int u = 0; u < kReduceAhead; ++u)
                 if (u < n) x[u] = load_raw<kLd>(a, r + u, j0);
 #pragma unroll
-            for (int u = 0; u < kAhead; ++u) {
+            for (int u = 0; u < kReduceAhead; ++u) {
                 if (u >= n) break;
                 const u4 v = finish<kLd>(x[u], a, r + u);
                 if (pos == 0) set8<kPre>(s, v, a); else add8<kPre>(s, v, a);
                 if (++pos == a.group) {
 #pragma unroll
-                    for (int e = 0; e < kEpt; ++e) acc[e] = have ? acc[e] + s[e] : s[e];
+                    for (int e = 0; e < 8; ++e) acc[e] = have ? acc[e] + s[e] : s[e];
                     have = true;
                     pos = 0;
                 }
             }
         }
-    }
-    if (a.last) {
-#pragma unroll
-        for (int e = 0; e < kEpt; ++e) acc[e] = acc[e] / a.post;
-        if constexpr (kAccum) {
-            float prev[kEpt];
-            load_out8(prev, a.out + j0);
-#pragma unroll
-            for (int e = 0; e < kEpt; ++e) acc[e] = prev[e] + acc[e];
-        }
-    }
-    if constexpr (kWhole) {
-        store_whole8(a.out + (j0 - 8 * static_cast<int64_t>(threadIdx.x & 63)), acc);
-    } else {
-        st4(a.out + j0, f4{acc[0], acc[1], acc[2], acc[3]});
-        st4(a.out + j0 + 4, f4{acc[4], acc[5], acc[6], acc[7]});
+        finish8<kAccum, kWhole, true>(a, j0, acc, s);
     }
 }
 
 // One tile of kReduceThreads * 8 outputs per workgroup.  Each lane owns 8
 // consecutive outputs; for every rank it loads their 8 bf16 as one 16-byte
-// vector (a wave reads 1 KiB contiguous per rank), kAhead ranks at a time, then
-// adds them strictly in rank order.  Hybrid: the same within each group of
+// vector (a wave reads 1 KiB contiguous per rank), kReduceAhead ranks at a time,
+// then adds them strictly in rank order.  Hybrid: the same within each group of
 // ranks, then the group sums in group order.  kLd: how contributions are read
 // (the output is 16-byte aligned unless kLd is kLdScalar).
 // The tile that the output's end cuts runs first (workgroup 0), so that its longer
@@ -741,13 +752,15 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 // its 512 outputs, so the waves in flight read from all ranks' rows at once (128
 // contribution rows on a 128-rank shard), and HBM serves that many scattered streams
 // more slowly than a few (read-only: 6.5 against 7.0 TB/s).  Here each wave owns kV
-// consecutive whole tiles (8 kV accumulators per lane) and walks the ranks in order,
-// loading rank r + 1's kV vectors while it adds rank r's; the host sizes the grid so
-// that every wave is resident at once, so the waves move through the ranks together
-// and HBM serves a few rows at a time.  Per output the operations and their order are
-// those of the tile path (flat sum, whole-dword contributions), so the results are
-// identical.  Block layout of a launch: the tile the output's end cuts (if any), then
-// n_single whole tiles that take the tile path, then the sweep waves.
+// consecutive whole tiles (8 kV sums per lane) and walks the ranks in order, loading
+// rank r + 1's kV vectors while it adds rank r's; the host sizes the grid so that
+// every wave is resident at once, so the waves move through the ranks together and
+// HBM serves a few rows at a time.  Per output the operations and their order are
+// those of the tile path (whole-dword contributions), so the results are identical.
+// Hybrid groups keep a second set of kV x 8 sums per lane (the group's), folded into
+// the total after each group's last rank; with the total's registers that allows
+// fewer tiles per wave.  Block layout of a launch: the tile the output's end cuts (if
+// any), then n_single whole tiles that take the tile path, then the sweep waves.
 struct SweepArgs {
     ReduceArgs r;
     int64_t t_first;   // first whole tile (512 outputs) of this launch
@@ -755,25 +768,39 @@ struct SweepArgs {
     int32_t n_single;  // then this many blocks reduce one whole tile each
 };
 
-template <int kPre, bool kAccum, int kV>
+template <int kPre, bool kAccum, bool kHybrid, int kV>
 __device__ __forceinline__ void sweep_wave(const ReduceArgs& a, int64_t t0) {
     constexpr int kTile = 512;
     const int lane = threadIdx.x & 63;
     // element offset of the lane's first vector from the run's start (vector v: + 512 v)
     const int64_t base = t0 * kTile;
     const int off = 8 * lane;
-    float acc[kV][8];
-    if (a.first) {
-        // -0 + t == t for every t (a NaN comes out quiet, as the divide by post makes
-        // it anyway), so adding rank 0 to -0 gives the tile path's first term
+    // The sums start from -0.0f: -0 + t == t for every t (a NaN comes out quiet, as the
+    // divide by post makes it anyway), so the first add gives the tile path's first
+    // assignment, for the flat sum, a group's sum and the total alike.
+    float acc[kV][8];                // the flat sum; hybrid: the total of completed groups
+    float s[kHybrid ? kV : 1][8];    // hybrid: the current group's sum
+    if (a.flags & kTIn) {
+#pragma unroll
+        for (int v = 0; v < kV; ++v) load_out8(acc[v], a.carry_t + base + off + kTile * v);
+    } else {
 #pragma unroll
         for (int v = 0; v < kV; ++v)
 #pragma unroll
             for (int e = 0; e < 8; ++e) acc[v][e] = -0.0f;
-    } else {
-#pragma unroll
-        for (int v = 0; v < kV; ++v) load_out8(acc[v], a.out + base + off + kTile * v);
     }
+    if constexpr (kHybrid) {
+        if (a.flags & kSIn) {
+#pragma unroll
+            for (int v = 0; v < kV; ++v) load_out8(s[v], a.carry_s + base + off + kTile * v);
+        } else {
+#pragma unroll
+            for (int v = 0; v < kV; ++v)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s[v][e] = -0.0f;
+        }
+    }
+    int pos = a.pos0;
     u4 x[kV];  // rank r's vectors
     const uint16_t* c0 = a.c[0] + base;
 #pragma unroll
@@ -783,32 +810,47 @@ __device__ __forceinline__ void sweep_wave(const ReduceArgs& a, int64_t t0) {
 #pragma unroll
         for (int v = 0; v < kV; ++v) {
             // one vector at a time, its adds before its reload: no second copy of any
-            // vector is live, so the wave holds 12 kV registers of data
-            add8<kPre>(acc[v], x[v], a);
+            // vector is live
+            if constexpr (kHybrid) add8<kPre>(s[v], x[v], a);
+            else add8<kPre>(acc[v], x[v], a);
             x[v] = ldu4w(cn + off + kTile * v);
             __builtin_amdgcn_sched_barrier(0);
         }
-    }
+        if constexpr (kHybrid) {
+            // a group that ends with rank r is folded into the total (wave-uniform)
+            if (++pos == a.group) {
 #pragma unroll
-    for (int v = 0; v < kV; ++v) add8<kPre>(acc[v], x[v], a);
+                for (int v = 0; v < kV; ++v)
 #pragma unroll
-    for (int v = 0; v < kV; ++v) {
-        float* o = a.out + base + kTile * v;
-        if (a.last) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) acc[v][e] = acc[v][e] / a.post;
-            if constexpr (kAccum) {
-                float prev[8];
-                load_out8(prev, o + off);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[v][e] = prev[e] + acc[v][e];
+                    for (int e = 0; e < 8; ++e) {
+                        acc[v][e] = acc[v][e] + s[v][e];
+                        s[v][e] = -0.0f;
+                    }
+                pos = 0;
             }
         }
-        store_whole8(o, acc[v]);
+    }
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+        if constexpr (kHybrid) add8<kPre>(s[v], x[v], a);
+        else add8<kPre>(acc[v], x[v], a);
+    }
+    if constexpr (kHybrid) {
+        if (++pos == a.group) {
+#pragma unroll
+            for (int v = 0; v < kV; ++v)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[v][e] = acc[v][e] + s[v][e];
+        }
+    }
+#pragma unroll
+    for (int v = 0; v < kV; ++v) {
+        if constexpr (kHybrid) finish8<kAccum, true, true>(a, base + off + kTile * v, acc[v], s[v]);
+        else finish8<kAccum, true, false>(a, base + off + kTile * v, acc[v], acc[v]);
     }
 }
 
-template <int kPre, bool kAccum, int kV>
+template <int kPre, bool kAccum, bool kHybrid, int kV>
 __global__ __launch_bounds__(64) void reduce_sweep_kernel(SweepArgs s) {
     const ReduceArgs& a = s.r;
     constexpr int64_t kTile = 512;
@@ -822,50 +864,59 @@ __global__ __launch_bounds__(64) void reduce_sweep_kernel(SweepArgs s) {
             // len % 8 outputs one lane each
             const int64_t t = a.len / kTile;
             const int64_t j0 = t * kTile + 8 * static_cast<int64_t>(threadIdx.x);
-            if (j0 + 8 <= a.len) reduce_lane<kPre, kLdWord, false, kAccum, false>(a, j0);
+            if (j0 + 8 <= a.len) reduce_lane<kPre, kLdWord, kHybrid, kAccum, false>(a, j0);
             const int64_t j = (a.len & ~int64_t{7}) + threadIdx.x;
-            if (j < a.len) reduce_one<kPre, false, kAccum>(a, j);
+            if (j < a.len) reduce_one<kPre, kHybrid, kAccum>(a, j);
             return;
         }
         --b;
     }
     if (b < s.n_single) {
-        reduce_lane<kPre, kLdWord, false, kAccum, true>(
+        reduce_lane<kPre, kLdWord, kHybrid, kAccum, true>(
             a, (s.t_first + b) * kTile + 8 * static_cast<int64_t>(threadIdx.x));
         return;
     }
-    sweep_wave<kPre, kAccum, kV>(a, s.t_first + s.n_single + (b - s.n_single) * kV);
+    sweep_wave<kPre, kAccum, kHybrid, kV>(a, s.t_first + s.n_single + (b - s.n_single) * kV);
 }
 
 // ---------------------------------------------------------------------------
 // local gradient accumulation (no communication): acc = (init ? 0 : acc) + fp32(g)
 // ---------------------------------------------------------------------------
+// One block of 8 * kThreads elements per workgroup, 512 per wave.  Each lane reads 8
+// consecutive bf16 with one 16-byte load (1 KiB per wave instruction), and the wave's fp32
+// accumulator with two 16-byte loads and two stores that each cover 1 KiB contiguous: in half
+// h, lane l takes elements 256h + 4l .. 256h + 4l + 3, whose bf16 lane 32h + l/2 holds
+// (exchanged across lanes with ds_bpermute, no LDS allocation).  Against 8-byte bf16 loads
+// with 4 elements per lane (4 per lane and vector, 4 vectors: 6.02-6.07 TB/s over the
+// GPT-175B unit's 1.8 G elements) this measured 6.32-6.34 TB/s; with 16-byte fp32 accesses
+// at a 32-byte stride instead of the exchange 5.32-5.52.  Grids of 2^18 blocks or more hand
+// each XCD runs of kAccXcdChunk blocks.
 template <bool kInit, bool kVec>
 __global__ __launch_bounds__(kThreads) void accumulate_kernel(const uint16_t* __restrict__ g,
                                                               float* __restrict__ acc,
                                                               int64_t len) {
-    constexpr int kV = FSDP_ACC_VPL;
-    constexpr int64_t kPerBlk = static_cast<int64_t>(kThreads) * 4 * kV;
-    const uint32_t blk = gridDim.x >= FSDP_XCD_MIN_TILES
-                             ? xcd_chunked<FSDP_ACC_XCD_CHUNK>(blockIdx.x, gridDim.x)
+    constexpr int64_t kPerBlk = static_cast<int64_t>(kThreads) * 8;
+    const uint32_t blk = gridDim.x >= kXcdMinTiles
+                             ? xcd_chunked<kAccXcdChunk>(blockIdx.x, gridDim.x)
                              : blockIdx.x;
     const int64_t base = static_cast<int64_t>(blk) * kPerBlk;
     if (kVec && base + kPerBlk <= len) {
-        // lane l owns elements [4l, 4l+4) of each of the tile's kV slices of 4 * kThreads
-        u2 x[kV];
-        f4 y[kV];
-#pragma unroll
-        for (int h = 0; h < kV; ++h) {
-            const int64_t o = base + 4 * (threadIdx.x + h * kThreads);
-            x[h] = __builtin_nontemporal_load(reinterpret_cast<const u2*>(g + o));
-            if constexpr (!kInit) y[h] = ld4s<FSDP_ACC_NT != 0>(acc + o);
+        const int lane = threadIdx.x & 63;
+        const int64_t wb = base + 512 * static_cast<int64_t>(threadIdx.x >> 6);
+        const u4 x = ldu4w(g + wb + 8 * lane);
+        f4 y[2];
+        if constexpr (!kInit) {
+            y[0] = ld4(acc + wb + 4 * lane);
+            y[1] = ld4(acc + wb + 256 + 4 * lane);
         }
 #pragma unroll
-        for (int h = 0; h < kV; ++h) {
-            const f4 w = {__builtin_bit_cast(float, x[h][0] << 16),
-                          __builtin_bit_cast(float, x[h][0] & 0xFFFF0000u),
-                          __builtin_bit_cast(float, x[h][1] << 16),
-                          __builtin_bit_cast(float, x[h][1] & 0xFFFF0000u)};
+        for (int h = 0; h < 2; ++h) {
+            const int src = 32 * h + (lane >> 1);
+            const uint32_t a0 = __shfl(x[0], src, 64), a1 = __shfl(x[1], src, 64);
+            const uint32_t b0 = __shfl(x[2], src, 64), b1 = __shfl(x[3], src, 64);
+            const uint32_t w0 = (lane & 1) ? b0 : a0, w1 = (lane & 1) ? b1 : a1;
+            const f4 w = {__builtin_bit_cast(float, w0 << 16), __builtin_bit_cast(float, w0 & 0xFFFF0000u),
+                          __builtin_bit_cast(float, w1 << 16), __builtin_bit_cast(float, w1 & 0xFFFF0000u)};
             f4 r;
             if constexpr (kInit) {
                 r = w;
@@ -873,11 +924,11 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(const uint16_t* __
 #pragma unroll
                 for (int q = 0; q < 4; ++q) r[q] = y[h][q] + w[q];
             }
-            st4s<FSDP_ACC_NT != 0>(acc + base + 4 * (threadIdx.x + h * kThreads), r);
+            st4(acc + wb + 256 * h + 4 * lane, r);
         }
         return;
     }
-    for (int e = 0; e < 4 * kV; ++e) {
+    for (int e = 0; e < 8; ++e) {
         const int64_t j = base + static_cast<int64_t>(e) * kThreads + threadIdx.x;
         if (j < len) {
             const float w = __builtin_bit_cast(float, static_cast<uint32_t>(g[j]) << 16);
@@ -921,8 +972,6 @@ __device__ __forceinline__ void adam_one(const AdamArgs& a, int64_t j) {
 // l + kAdamThreads (4 elements each) of every array.
 template <bool kVec, bool kBf16>
 __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
-    constexpr bool kNTL = FSDP_ADAM_NT_LOAD != 0;
-    constexpr bool kNTS = FSDP_ADAM_NT_STORE != 0;
     constexpr int64_t kPerBlk = static_cast<int64_t>(kAdamThreads) * 8;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kPerBlk;
     if constexpr (kVec) {
@@ -931,10 +980,10 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int64_t o = base + 4 * (threadIdx.x + h * kAdamThreads);
-                p[h] = ld4s<kNTL>(a.p + o);
-                g[h] = ld4s<kNTL>(a.g + o);
-                m[h] = ld4s<kNTL>(a.m + o);
-                v[h] = ld4s<kNTL>(a.v + o);
+                p[h] = *reinterpret_cast<const f4*>(a.p + o);
+                g[h] = *reinterpret_cast<const f4*>(a.g + o);
+                m[h] = *reinterpret_cast<const f4*>(a.m + o);
+                v[h] = *reinterpret_cast<const f4*>(a.v + o);
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -947,31 +996,18 @@ __global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
                     v[h][q] = vv;
                 }
             }
-#if FSDP_ADAM_STORE_CPOL
             const auto rp = block_rsrc(a.p + base, kPerBlk * 4), rm = block_rsrc(a.m + base, kPerBlk * 4),
                        rv = block_rsrc(a.v + base, kPerBlk * 4);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const int o = 16 * (threadIdx.x + h * kAdamThreads);
-                bst4<FSDP_ADAM_STORE_CPOL>(rp, o, p[h]);
-                bst4<FSDP_ADAM_STORE_CPOL>(rm, o, m[h]);
-                bst4<FSDP_ADAM_STORE_CPOL>(rv, o, v[h]);
+                bst4<kAdamStoreCpol>(rp, o, p[h]);
+                bst4<kAdamStoreCpol>(rm, o, m[h]);
+                bst4<kAdamStoreCpol>(rv, o, v[h]);
                 if constexpr (kBf16)
-                    bst2<FSDP_ADAM_STORE_CPOL>(block_rsrc(a.pb + base, kPerBlk * 2), o / 2,
-                                                 u2{pack_bf16x2(p[h][0], p[h][1]),
-                                                    pack_bf16x2(p[h][2], p[h][3])});
+                    bst2<kAdamStoreCpol>(block_rsrc(a.pb + base, kPerBlk * 2), o / 2,
+                                         u2{pack_bf16x2(p[h][0], p[h][1]), pack_bf16x2(p[h][2], p[h][3])});
             }
-#else
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int64_t o = base + 4 * (threadIdx.x + h * kAdamThreads);
-                st4s<kNTS>(a.p + o, p[h]);
-                st4s<kNTS>(a.m + o, m[h]);
-                st4s<kNTS>(a.v + o, v[h]);
-                if constexpr (kBf16)
-                    stu2(a.pb + o, u2{pack_bf16x2(p[h][0], p[h][1]), pack_bf16x2(p[h][2], p[h][3])});
-            }
-#endif
             return;
         }
     }
@@ -990,13 +1026,29 @@ bool aligned_to(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t
 // Grid of `tiles` workgroups, one tile each (checked < 2^31 by the callers).
 dim3 grid_of(int64_t tiles) { return dim3(static_cast<unsigned>(std::max<int64_t>(1, tiles))); }
 
+// Launch with the smallest table that holds the launch's segments.
+template <typename SrcT, typename DstT, int kCap>
+void launch_table(const SegTable<kMaxSegs>& full, bool general, uint64_t tiles, hipStream_t stream) {
+    SegTable<kCap> t{};
+    t.ntiles = full.ntiles;
+    t.nseg = full.nseg;
+    t.xcd_runs = full.xcd_runs;
+    for (uint32_t i = 0; i < full.nseg; ++i) t.seg[i] = full.seg[i];
+    if (general)
+        hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, true, kCap>), grid_of(tiles), dim3(kThreads), 0,
+                           stream, t);
+    else
+        hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, false, kCap>), grid_of(tiles), dim3(kThreads), 0,
+                           stream, t);
+}
+
 template <typename SrcT, typename DstT>
 hipError_t launch_segcopy_t(const std::vector<CopySeg>& segs, hipStream_t stream) {
     constexpr int64_t kTile = tile_elems<SrcT, DstT>();
     constexpr uintptr_t kDstAlign = Cp<SrcT, DstT>::kDstAlign;
     size_t i = 0;
     while (i < segs.size()) {
-        SegTable t{};
+        SegTable<kMaxSegs> t{};
         uint64_t tiles = 0;
         bool general = false;
         for (; i < segs.size() && t.nseg < static_cast<uint32_t>(kMaxSegs); ++i) {
@@ -1027,13 +1079,11 @@ hipError_t launch_segcopy_t(const std::vector<CopySeg>& segs, hipStream_t stream
         }
         if (t.nseg == 0) continue;
         t.ntiles = static_cast<uint32_t>(tiles);
-        t.xcd_runs = tiles >= FSDP_XCD_MIN_TILES ? 1u : 0u;
-        if (general)
-            hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, true>), grid_of(tiles), dim3(kThreads),
-                               0, stream, t);
-        else
-            hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, false>), grid_of(tiles), dim3(kThreads),
-                               0, stream, t);
+        t.xcd_runs = tiles >= kXcdMinTiles ? 1u : 0u;
+        if (t.nseg <= 1) launch_table<SrcT, DstT, 1>(t, general, tiles, stream);
+        else if (t.nseg <= 4) launch_table<SrcT, DstT, 4>(t, general, tiles, stream);
+        else if (t.nseg <= 16) launch_table<SrcT, DstT, 16>(t, general, tiles, stream);
+        else launch_table<SrcT, DstT, kMaxSegs>(t, general, tiles, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1062,7 +1112,7 @@ void launch_reduce_mode(const ReduceArgs& a, bool hybrid, bool accum, dim3 grid,
 template <bool kVec>
 __global__ __launch_bounds__(kThreads) void unscale_kernel(float* __restrict__ g, int64_t len,
                                                            float inv, float* __restrict__ found) {
-    constexpr int kV = FSDP_UNSCALE_VPL;
+    constexpr int kV = kUnscaleVpl;
     constexpr int64_t kPerBlk = static_cast<int64_t>(kThreads) * 4 * kV;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kPerBlk;
     bool bad = false;
@@ -1192,12 +1242,12 @@ hipError_t launch_segcopy(const std::vector<CopySeg>& segs, Pipe pipe, hipStream
     return hipErrorInvalidValue;
 }
 
-// Workgroups of reduce_sweep_kernel<kPre, kAccum, kSweepV> resident at once on the
-// current device (occupancy per CU times CUs), queried once per device; 0 if unknown.
-constexpr int kSweepV = FSDP_SWEEP_V;
+// Workgroups of a reduce_sweep_kernel instantiation resident at once on the current device
+// (occupancy per CU times CUs), queried once per device; 0 if unknown.
 constexpr int kMaxDevices = 64;
-template <int kPre, bool kAccum>
+template <int kPre, bool kAccum, bool kHybrid>
 int64_t sweep_capacity() {
+    constexpr int kV = kHybrid ? kHybridSweepV : kSweepV;
     static std::atomic<int64_t> cap[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
@@ -1205,7 +1255,7 @@ int64_t sweep_capacity() {
     if (c == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(&reduce_sweep_kernel<kPre, kAccum, kSweepV>),
+                &per_cu, reinterpret_cast<const void*>(&reduce_sweep_kernel<kPre, kAccum, kHybrid, kV>),
                 64, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -1215,16 +1265,17 @@ int64_t sweep_capacity() {
     return c > 0 ? c : 0;
 }
 
-// The sweep over this launch's ranks, one launch per run of plan_sweep_runs (runs whose
+// The sweep over one launch's ranks, one kernel launch per run of plan_sweep_runs (runs whose
 // grids are resident at once), in output order; *err gets the first launch error.  Returns
-// false, having launched nothing, when the output is too short or the occupancy unknown.
-template <int kPre, bool kAccum>
+// false, having launched nothing, when the output holds fewer whole tiles than a sweep wave
+// or the occupancy is unknown.
+template <int kPre, bool kAccum, bool kHybrid>
 bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
+    constexpr int kV = kHybrid ? kHybridSweepV : kSweepV;
     constexpr int64_t kTile = 512;
-    const int64_t tiles = a.len / kTile;
-    if (tiles < FSDP_SWEEP_MIN_TILES) return false;
     std::vector<SweepRun> runs;
-    if (!plan_sweep_runs(tiles, a.len % kTile != 0, kSweepV, sweep_capacity<kPre, kAccum>(), &runs))
+    if (!plan_sweep_runs(a.len / kTile, a.len % kTile != 0, kV,
+                         sweep_capacity<kPre, kAccum, kHybrid>(), &runs))
         return false;
     for (const SweepRun& r : runs) {
         SweepArgs s{};
@@ -1232,7 +1283,7 @@ bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
         s.t_first = r.t_first;
         s.cut = r.cut;
         s.n_single = r.n_single;
-        hipLaunchKernelGGL((reduce_sweep_kernel<kPre, kAccum, kSweepV>),
+        hipLaunchKernelGGL((reduce_sweep_kernel<kPre, kAccum, kHybrid, kV>),
                            dim3(static_cast<unsigned>(r.blocks)), dim3(64), 0, stream, s);
         *err = hipGetLastError();
         if (*err != hipSuccess) break;
@@ -1240,26 +1291,42 @@ bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
     return true;
 }
 
-// The sweep, for a flat sum over at least FSDP_SWEEP_MIN_RANKS contributions that are all
-// at least 4-byte aligned into a 16-byte-aligned output; false if it does not apply.
-bool launch_reduce_sweep(const ReduceArgs& a, int mode, bool accum, hipStream_t stream,
+template <int kPre>
+bool launch_reduce_sweep(const ReduceArgs& a, bool hybrid, bool accum, hipStream_t stream,
                          hipError_t* err) {
-    if (a.nc < FSDP_SWEEP_MIN_RANKS) return false;
-    if (mode == kPreNone)
-        return accum ? try_sweep<kPreNone, true>(a, stream, err) : try_sweep<kPreNone, false>(a, stream, err);
-    if (mode == kPreRecip)
-        return accum ? try_sweep<kPreRecip, true>(a, stream, err) : try_sweep<kPreRecip, false>(a, stream, err);
-    return accum ? try_sweep<kPreDiv, true>(a, stream, err) : try_sweep<kPreDiv, false>(a, stream, err);
+    if (hybrid)
+        return accum ? try_sweep<kPre, true, true>(a, stream, err) : try_sweep<kPre, false, true>(a, stream, err);
+    return accum ? try_sweep<kPre, true, false>(a, stream, err) : try_sweep<kPre, false, false>(a, stream, err);
+}
+
+template <int kPre>
+void launch_reduce_tiles(const ReduceArgs& a, int ld, bool hybrid, bool accum, dim3 grid,
+                         hipStream_t stream) {
+    if (ld == kLdWord) launch_reduce_mode<kPre, kLdWord>(a, hybrid, accum, grid, stream);
+    else if (ld == kLdHalf) launch_reduce_mode<kPre, kLdHalf>(a, hybrid, accum, grid, stream);
+    else launch_reduce_mode<kPre, kLdScalar>(a, hybrid, accum, grid, stream);
+}
+
+int64_t reduce_workspace_floats(int64_t n_contrib, int64_t len, int64_t group, bool accumulate) {
+    if (len <= 0 || n_contrib <= 0) return 0;
+    ReducePlan plan;
+    plan_reduce(n_contrib, group, accumulate, kMaxContrib, &plan);
+    return plan.ws_slots * reduce_ws_pitch(len);
 }
 
 hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib, int64_t len,
                               float pre, float post, int64_t group, bool accumulate, float* out,
-                              hipStream_t stream) {
+                              float* workspace, ReduceKernel kernel, hipStream_t stream) {
     if (len <= 0 || n_contrib <= 0) return hipSuccess;
     // one group of all ranks, or groups of one, are the flat sequential sum
     const bool hybrid = group > 1 && group < n_contrib;
-    if (hybrid && (n_contrib % group != 0 || group > kMaxContrib)) return hipErrorInvalidValue;
-    if (accumulate && n_contrib > kMaxContrib) return hipErrorInvalidValue;
+    if (hybrid && n_contrib % group != 0) return hipErrorInvalidValue;
+    ReducePlan plan;
+    plan_reduce(n_contrib, group, accumulate, kMaxContrib, &plan);
+    if (plan.ws_slots > 0 && workspace == nullptr) return hipErrorInvalidValue;
+    const int64_t pitch = reduce_ws_pitch(len);
+    float* carry_t = plan.t_slot < 0 ? out : workspace + plan.t_slot * pitch;
+    float* carry_s = plan.s_slot < 0 ? nullptr : workspace + plan.s_slot * pitch;
     int mode = kPreDiv;
     float rpre = 1.0f;
     if (pre == 1.0f) {
@@ -1270,48 +1337,48 @@ hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib
         rpre = 1.0f / pre;
         if (mant == 0.5f && std::isnormal(rpre) && rpre * pre == 1.0f) mode = kPreRecip;
     }
-    // vector path when the output is 16-byte aligned; contributions only 2-byte
-    // aligned are read one element early and shifted
+    // vector path when the output (and the workspace) is 16-byte aligned; contributions
+    // only 2-byte aligned are read one element early and shifted
     bool all4 = true;
     for (int64_t r = 0; r < n_contrib; ++r) all4 = all4 && aligned_to(contribs[r], 4);
-    const int ld = !aligned_to(out, 16) ? kLdScalar : all4 ? kLdWord : kLdHalf;
+    const bool vec_out = aligned_to(out, 16) && (workspace == nullptr || aligned_to(workspace, 16));
+    const int ld = !vec_out ? kLdScalar : all4 ? kLdWord : kLdHalf;
     const int64_t per_blk = static_cast<int64_t>(kReduceThreads) * 8;
     const int64_t blocks = (len + per_blk - 1) / per_blk;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    // a launch holds up to kMaxContrib ranks; hybrid launches hold whole groups, so
-    // the running value carried in `out` between launches is always a complete sum
-    const int64_t chunk = hybrid ? (kMaxContrib / group) * group : kMaxContrib;
-    for (int64_t r0 = 0; r0 < n_contrib; r0 += chunk) {
+    const int64_t whole_tiles = len / per_blk;
+    for (const ReduceLaunch& l : plan.launches) {
         ReduceArgs a{};
-        a.nc = static_cast<int32_t>(std::min<int64_t>(chunk, n_contrib - r0));
-        for (int32_t r = 0; r < a.nc; ++r) a.c[r] = contribs[r0 + r];
+        a.nc = static_cast<int32_t>(l.nc);
+        for (int32_t r = 0; r < a.nc; ++r) a.c[r] = contribs[l.r0 + r];
         a.out = out;
+        a.carry_t = carry_t;
+        a.carry_s = carry_s;
         a.len = len;
-        a.group = static_cast<int32_t>(hybrid ? group : a.nc);
-        a.first = r0 == 0;
-        a.last = r0 + a.nc == n_contrib;
+        a.group = static_cast<int32_t>(hybrid ? group : n_contrib);
+        a.pos0 = static_cast<int32_t>(l.pos0);
+        a.flags = l.flags;
         a.pre = pre;
         a.rpre = rpre;
         a.post = post;
-        const dim3 grid = grid_of(blocks);
-        hipError_t swept = hipSuccess;
-        if (!hybrid && ld == kLdWord && launch_reduce_sweep(a, mode, accumulate, stream, &swept)) {
+        // the row-major sweep where its loads apply (whole dwords); by default only where it
+        // measured faster: many ranks in the launch and a long output
+        const bool sweep = ld == kLdWord && kernel != ReduceKernel::kTiles &&
+                           (kernel == ReduceKernel::kSweep ||
+                            (a.nc >= kSweepMinRanks && whole_tiles >= kSweepMinTiles));
+        if (sweep) {
+            hipError_t swept = hipSuccess;
+            bool ran = false;
+            if (mode == kPreNone) ran = launch_reduce_sweep<kPreNone>(a, hybrid, accumulate, stream, &swept);
+            else if (mode == kPreRecip) ran = launch_reduce_sweep<kPreRecip>(a, hybrid, accumulate, stream, &swept);
+            else ran = launch_reduce_sweep<kPreDiv>(a, hybrid, accumulate, stream, &swept);
             if (swept != hipSuccess) return swept;
-            continue;
+            if (ran) continue;
         }
-        if (mode == kPreNone) {
-            if (ld == kLdWord) launch_reduce_mode<kPreNone, kLdWord>(a, hybrid, accumulate, grid, stream);
-            else if (ld == kLdHalf) launch_reduce_mode<kPreNone, kLdHalf>(a, hybrid, accumulate, grid, stream);
-            else launch_reduce_mode<kPreNone, kLdScalar>(a, hybrid, accumulate, grid, stream);
-        } else if (mode == kPreRecip) {
-            if (ld == kLdWord) launch_reduce_mode<kPreRecip, kLdWord>(a, hybrid, accumulate, grid, stream);
-            else if (ld == kLdHalf) launch_reduce_mode<kPreRecip, kLdHalf>(a, hybrid, accumulate, grid, stream);
-            else launch_reduce_mode<kPreRecip, kLdScalar>(a, hybrid, accumulate, grid, stream);
-        } else {
-            if (ld == kLdWord) launch_reduce_mode<kPreDiv, kLdWord>(a, hybrid, accumulate, grid, stream);
-            else if (ld == kLdHalf) launch_reduce_mode<kPreDiv, kLdHalf>(a, hybrid, accumulate, grid, stream);
-            else launch_reduce_mode<kPreDiv, kLdScalar>(a, hybrid, accumulate, grid, stream);
-        }
+        const dim3 grid = grid_of(blocks);
+        if (mode == kPreNone) launch_reduce_tiles<kPreNone>(a, ld, hybrid, accumulate, grid, stream);
+        else if (mode == kPreRecip) launch_reduce_tiles<kPreRecip>(a, ld, hybrid, accumulate, grid, stream);
+        else launch_reduce_tiles<kPreDiv>(a, ld, hybrid, accumulate, grid, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1321,10 +1388,11 @@ hipError_t launch_grad_reduce(const uint16_t* const* contribs, int64_t n_contrib
 hipError_t launch_grad_accumulate(const uint16_t* grad, float* acc, int64_t len, bool init,
                                   hipStream_t stream) {
     if (len <= 0) return hipSuccess;
-    const int64_t per_blk = static_cast<int64_t>(kThreads) * 4 * FSDP_ACC_VPL;
+    const int64_t per_blk = static_cast<int64_t>(kThreads) * 8;
     const int64_t blocks = (len + per_blk - 1) / per_blk;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
-    const bool vec = aligned_to(grad, 8) && aligned_to(acc, 16);
+    // 16-byte bf16 loads need dword alignment only
+    const bool vec = aligned_to(grad, 4) && aligned_to(acc, 16);
     const dim3 grid = grid_of(blocks), block(kThreads);
     if (init) {
         if (vec) hipLaunchKernelGGL((accumulate_kernel<true, true>), grid, block, 0, stream, grad, acc, len);
@@ -1362,7 +1430,7 @@ hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* 
 hipError_t launch_grad_unscale(float* g, int64_t len, float inv_scale, float* found_inf,
                                hipStream_t stream) {
     if (len <= 0) return hipSuccess;
-    const int64_t per_blk = static_cast<int64_t>(kThreads) * 4 * FSDP_UNSCALE_VPL;
+    const int64_t per_blk = static_cast<int64_t>(kThreads) * 4 * kUnscaleVpl;
     const int64_t blocks = (len + per_blk - 1) / per_blk;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const dim3 grid = grid_of(blocks), block(kThreads);

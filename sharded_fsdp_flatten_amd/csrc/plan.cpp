@@ -349,4 +349,47 @@ bool plan_sweep_runs(int64_t tiles, bool cut_tile, int64_t kv, int64_t capacity,
     return true;
 }
 
+void plan_reduce(int64_t n, int64_t group, bool accumulate, int64_t cap, ReducePlan* plan) {
+    plan->launches.clear();
+    const bool hybrid = group > 1 && group < n;
+    const int64_t F = hybrid ? group : n;
+    if (!hybrid || F <= cap) {
+        // every launch holds whole groups: only the total crosses launches
+        const int64_t chunk = hybrid ? (cap / F) * F : cap;
+        for (int64_t r0 = 0; r0 < n; r0 += chunk) {
+            ReduceLaunch l;
+            l.r0 = r0;
+            l.nc = std::min(chunk, n - r0);
+            const bool last = r0 + l.nc == n;
+            l.flags = (r0 > 0 ? kReduceTIn : 0u) | (last ? kReduceLast : kReduceTOut);
+            plan->launches.push_back(l);
+        }
+        const bool multi = plan->launches.size() > 1;
+        plan->t_slot = multi && accumulate ? 0 : -1;
+        plan->s_slot = -1;
+        plan->ws_slots = multi && accumulate ? 1 : 0;
+        return;
+    }
+    // groups longer than a launch: each takes launches of its own; a group's partial sum
+    // crosses them, and the total is loaded and stored only by a group's last launch
+    const int64_t groups = n / F;
+    for (int64_t g = 0; g < groups; ++g)
+        for (int64_t p0 = 0; p0 < F; p0 += cap) {
+            ReduceLaunch l;
+            l.r0 = g * F + p0;
+            l.nc = std::min(cap, F - p0);
+            l.pos0 = p0;
+            const bool completes = p0 + l.nc == F;
+            const bool last = completes && g + 1 == groups;
+            l.flags = (p0 > 0 ? kReduceSIn : 0u) | (completes && g > 0 ? kReduceTIn : 0u) |
+                      (last ? kReduceLast : completes ? kReduceTOut : kReduceSOut);
+            plan->launches.push_back(l);
+        }
+    plan->t_slot = accumulate ? 0 : -1;
+    plan->s_slot = accumulate ? 1 : 0;
+    plan->ws_slots = accumulate ? 2 : 1;
+}
+
+int64_t reduce_ws_pitch(int64_t S) { return (S + 63) / 64 * 64; }
+
 }  // namespace fsdp

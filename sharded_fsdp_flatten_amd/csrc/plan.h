@@ -97,4 +97,41 @@ struct SweepRun {
 bool plan_sweep_runs(int64_t tiles, bool cut_tile, int64_t kv, int64_t capacity,
                      std::vector<SweepRun>* runs);
 
+// A reduction over more ranks than one launch's pointer table holds (`cap`) takes several
+// launches in rank order.  Between them the running sums sit in HBM, stored exactly: the
+// total (the flat sum, or the sum of the completed groups) and, when a group is longer
+// than one launch, that group's partial sum.  Each launch's flags say what it loads and
+// stores.
+enum ReduceFlag : uint32_t {
+    kReduceTIn = 1u,    // the total so far is carried in (else it starts in this launch)
+    kReduceSIn = 2u,    // the partial sum of this launch's first group is carried in
+    kReduceTOut = 4u,   // not the last launch: the total is carried out
+    kReduceSOut = 8u,   // not the last launch: the last group's partial sum is carried out
+    kReduceLast = 16u,  // the last launch: total / post (+ the old value) is the result
+};
+struct ReduceLaunch {
+    int64_t r0 = 0;     // first rank
+    int64_t nc = 0;     // ranks
+    int64_t pos0 = 0;   // position of rank r0 in its group
+    uint32_t flags = 0;
+};
+struct ReducePlan {
+    std::vector<ReduceLaunch> launches;
+    // Where the carried sums live: -1 the output itself, else that slot of the caller's
+    // workspace (slot i starts i * reduce_ws_pitch(S) floats in).  The total is carried in
+    // the output unless the result is accumulated into it (the output then keeps the old
+    // value until the last launch).
+    int t_slot = -1;
+    int s_slot = -1;
+    int ws_slots = 0;   // workspace slots the plan uses
+};
+// Groups of `group` consecutive ranks (group <= 1 or >= n: one flat sum), at most `cap`
+// ranks per launch.  Groups that fit a launch are never split: a launch holds whole groups
+// (as many as fit); a longer group takes ceil(group / cap) launches of its own.
+// n >= 1, cap >= 1; group divides n when 1 < group < n.
+void plan_reduce(int64_t n, int64_t group, bool accumulate, int64_t cap, ReducePlan* plan);
+// Floats between workspace slots for a shard of S elements: S rounded up to 64 (256 bytes),
+// so every slot of a 16-byte-aligned workspace is 16-byte aligned.
+int64_t reduce_ws_pitch(int64_t S);
+
 }  // namespace fsdp

@@ -4,6 +4,7 @@
  * fail validation before any HIP call.  Prints "ok" and exits 0 when every check holds. */
 #include "fsdp_flatten.h"
 
+#include <stdint.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -58,9 +59,64 @@ int main(void) {
             CHECK(fsdp_adam_shard(u, NULL, NULL, NULL, NULL, &cfg, NULL, NULL) == FSDP_E_RANGE);
         }
         {
-            const fsdp_reduce_opts o = {1.0f, 1.0f, 3, 0}; /* 3 does not divide 16 */
+            fsdp_reduce_opts o;
+            int64_t n = -1;
+            memset(&o, 0, sizeof o);
+            o.pre_divide = 1.0f;
+            o.post_divide = 1.0f;
+            o.group = 3; /* 3 does not divide 16 */
+            CHECK(fsdp_grad_reduce_shard_ex(u, NULL, &o, NULL, NULL) == FSDP_E_RANGE);
+            CHECK(fsdp_grad_reduce_workspace(u, &o, &n) == FSDP_E_RANGE);
+            o.group = 4;
+            o.accumulate = 1;
+            CHECK(fsdp_grad_reduce_workspace(u, &o, &n) == FSDP_OK && n == 0);
+            o.kernel = 3; /* not an fsdp_reduce_kernel */
             CHECK(fsdp_grad_reduce_shard_ex(u, NULL, &o, NULL, NULL) == FSDP_E_RANGE);
         }
+        CHECK(fsdp_unit_destroy(u) == FSDP_OK);
+    }
+
+    /* 512 ranks (one launch holds 128): a [512, 3] parameter, S = 3.  The workspace holds
+     * the sums carried between launches in slots of S rounded up to 64 floats: one when the
+     * output keeps its old value (accumulate) or a group spans launches, two for both. */
+    {
+        const int32_t ndims[1] = {2};
+        const int64_t dims[2] = {512, 3};
+        fsdp_unit* u = NULL;
+        fsdp_reduce_opts o;
+        int64_t n = -1;
+        uint16_t* fake_contribs[512];
+        float* fake_out = (float*)(uintptr_t)0x100000;
+        int r;
+        memset(&o, 0, sizeof o);
+        o.pre_divide = 16.0f;
+        o.post_divide = 32.0f;
+        CHECK(fsdp_unit_create(FSDP_FLAT, 1, ndims, dims, 512, &u) == FSDP_OK);
+        CHECK(info(u, FSDP_ALL_RANKS).S == 3);
+        CHECK(fsdp_grad_reduce_workspace(u, &o, &n) == FSDP_OK && n == 0);
+        o.accumulate = 1;
+        CHECK(fsdp_grad_reduce_workspace(u, &o, &n) == FSDP_OK && n == 64);
+        o.group = 8;
+        CHECK(fsdp_grad_reduce_workspace(u, &o, &n) == FSDP_OK && n == 64);
+        o.group = 256;
+        CHECK(fsdp_grad_reduce_workspace(u, &o, &n) == FSDP_OK && n == 128);
+        o.accumulate = 0;
+        CHECK(fsdp_grad_reduce_workspace(u, &o, &n) == FSDP_OK && n == 64);
+        o.group = 8;
+        CHECK(fsdp_grad_reduce_workspace(u, &o, &n) == FSDP_OK && n == 0);
+        /* workspace errors are found before any HIP call (the pointers are never used) */
+        for (r = 0; r < 512; ++r) fake_contribs[r] = (uint16_t*)(uintptr_t)(0x200000 + 64 * r);
+        o.group = 256;
+        CHECK(fsdp_grad_reduce_shard_ex(u, (const uint16_t* const*)fake_contribs, &o, fake_out,
+                                        NULL) == FSDP_E_ARG);
+        o.workspace = (float*)(uintptr_t)0x300008;
+        o.workspace_len = 64;
+        CHECK(fsdp_grad_reduce_shard_ex(u, (const uint16_t* const*)fake_contribs, &o, fake_out,
+                                        NULL) == FSDP_E_ALIGN);
+        o.workspace = (float*)(uintptr_t)0x300000;
+        o.workspace_len = 63;
+        CHECK(fsdp_grad_reduce_shard_ex(u, (const uint16_t* const*)fake_contribs, &o, fake_out,
+                                        NULL) == FSDP_E_RANGE);
         CHECK(fsdp_unit_destroy(u) == FSDP_OK);
     }
 

@@ -8,9 +8,12 @@
 // [kS, (k+1)S); FSDP2 segment = per parameter the rows of the rank's torch.chunk chunk,
 // then zero rows up to the chunk size.  It also checks the per-parameter runs of a rank's
 // shard and that oversized units are rejected as overflows, not wrapped.
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
+#include <limits>
 #include <random>
 #include <string>
 #include <vector>
@@ -264,6 +267,109 @@ void check_sweep_runs(std::mt19937_64& rng, int iters) {
 
 }  // namespace
 
+// The reduction's launch plans: for random rank counts, group sizes, launch capacities and
+// accumulation, run the plan the way the kernels do -- each launch loads what its flags
+// say it carries in, adds its ranks in order (a group's sum starting at its first rank and
+// folded into the total after its last), and stores what it carries out, in binary32 --
+// with an unwritten workspace (NaN) and the old value in the output, and compare the result
+// bit for bit with one sequential pass over all ranks.  Also checks the structure: every
+// rank once and in order, at most cap ranks per launch, whole groups per launch when a
+// group fits one, the flags of the first and last launches, and the workspace slots.
+uint32_t bits(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    return u;
+}
+
+void check_reduce_plans(std::mt19937_64& rng, int iters) {
+    std::normal_distribution<float> nd(0.0f, 1.0f);
+    for (int it = 0; it < iters; ++it) {
+        const int64_t n = 1 + static_cast<int64_t>(rng() % (it % 3 == 0 ? 700 : 140));
+        std::vector<int64_t> divisors = {0};
+        for (int64_t d = 1; d <= n; ++d)
+            if (n % d == 0) divisors.push_back(d);
+        const int64_t group = divisors[rng() % divisors.size()];
+        const int64_t cap = it % 4 == 0 ? 128 : 1 + static_cast<int64_t>(rng() % 130);
+        const bool accumulate = rng() % 2 == 0;
+        fsdp::ReducePlan plan;
+        fsdp::plan_reduce(n, group, accumulate, cap, &plan);
+        const bool hybrid = group > 1 && group < n;
+        const int64_t F = hybrid ? group : n;
+        // structure
+        CHECK(!plan.launches.empty(), "reduce plan has launches");
+        int64_t next = 0;
+        for (size_t i = 0; i < plan.launches.size(); ++i) {
+            const fsdp::ReduceLaunch& l = plan.launches[i];
+            CHECK(l.r0 == next && l.nc >= 1 && l.nc <= cap, "launch ranks in order within cap");
+            CHECK(!hybrid || l.pos0 == l.r0 % F, "launch pos0 is the rank's place in its group");
+            if (hybrid && F <= cap) CHECK(l.r0 % F == 0 && l.nc % F == 0, "whole groups per launch");
+            const bool last = i + 1 == plan.launches.size();
+            CHECK(((l.flags & fsdp::kReduceLast) != 0) == last, "only the last launch finishes");
+            if (i == 0) CHECK((l.flags & (fsdp::kReduceTIn | fsdp::kReduceSIn)) == 0, "first launch carries nothing in");
+            next = l.r0 + l.nc;
+        }
+        CHECK(next == n, "every rank reduced");
+        CHECK(plan.ws_slots >= 0 && plan.ws_slots <= 2 && plan.t_slot < plan.ws_slots &&
+                  plan.s_slot < plan.ws_slots, "workspace slots in range");
+        if (accumulate && plan.launches.size() > 1) CHECK(plan.t_slot >= 0, "old value kept");
+        // values: a few outputs, terms of mixed magnitude so that the order matters
+        constexpr int kOut = 3;
+        const float post = (rng() % 2) ? 3.0f : 8.0f;
+        std::vector<float> t(static_cast<size_t>(n * kOut));
+        for (float& x : t) x = nd(rng) * std::ldexp(1.0f, static_cast<int>(rng() % 24) - 12);
+        float old[kOut], want[kOut];
+        for (int j = 0; j < kOut; ++j) {
+            old[j] = nd(rng);
+            float total = 0.0f;
+            for (int64_t g = 0; g < n / F; ++g) {
+                float sg = t[static_cast<size_t>(g * F * kOut + j)];
+                for (int64_t r = g * F + 1; r < (g + 1) * F; ++r) sg = sg + t[static_cast<size_t>(r * kOut + j)];
+                total = g == 0 ? sg : total + sg;
+            }
+            const float fresh = total / post;
+            want[j] = accumulate ? old[j] + fresh : fresh;
+        }
+        const float nan = std::numeric_limits<float>::quiet_NaN();
+        std::vector<float> out(old, old + kOut), ws(static_cast<size_t>(2 * kOut), nan);
+        float* carry_t = plan.t_slot < 0 ? out.data() : ws.data() + plan.t_slot * kOut;
+        float* carry_s = plan.s_slot < 0 ? nullptr : ws.data() + plan.s_slot * kOut;
+        for (const fsdp::ReduceLaunch& l : plan.launches) {
+            for (int j = 0; j < kOut; ++j) {
+                bool have = (l.flags & fsdp::kReduceTIn) != 0;
+                float acc = have ? carry_t[j] : nan;
+                float sg = (l.flags & fsdp::kReduceSIn) ? carry_s[j] : nan;
+                int64_t pos = l.pos0;
+                for (int64_t r = l.r0; r < l.r0 + l.nc; ++r) {
+                    const float x = t[static_cast<size_t>(r * kOut + j)];
+                    if (!hybrid) {
+                        acc = have ? acc + x : x;
+                        have = true;
+                    } else {
+                        sg = pos == 0 ? x : sg + x;
+                        if (++pos == F) {
+                            acc = have ? acc + sg : sg;
+                            have = true;
+                            pos = 0;
+                        }
+                    }
+                }
+                if (l.flags & fsdp::kReduceLast) {
+                    acc = acc / post;
+                    out[static_cast<size_t>(j)] = accumulate ? out[static_cast<size_t>(j)] + acc : acc;
+                } else {
+                    if (l.flags & fsdp::kReduceTOut) carry_t[j] = acc;
+                    if (l.flags & fsdp::kReduceSOut) {
+                        CHECK(carry_s != nullptr, "a carried group sum has a slot");
+                        if (carry_s) carry_s[j] = sg;
+                    }
+                }
+            }
+        }
+        for (int j = 0; j < kOut; ++j)
+            CHECK(bits(out[static_cast<size_t>(j)]) == bits(want[j]), "planned reduction equals the sequential one");
+    }
+}
+
 int main(int argc, char** argv) {
     const int iters = argc > 1 ? std::atoi(argv[1]) : 400;
     std::mt19937_64 rng(12345);
@@ -275,6 +381,7 @@ int main(int argc, char** argv) {
     }
     check_overflow();
     check_sweep_runs(rng, 20 * iters);
+    check_reduce_plans(rng, 10 * iters);
     if (g_fail) {
         std::fprintf(stderr, "%d failures\n", g_fail);
         return 1;

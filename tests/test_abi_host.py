@@ -2,6 +2,7 @@
 plans units exactly as the oracle lays them out, keeps the pages' memory ledger,
 and rejects every invalid argument before making any HIP call (so all of this
 runs without a GPU)."""
+import ctypes
 import os
 import re
 
@@ -330,13 +331,38 @@ def test_reduce_ex_errors(B):
             B.fsdp_grad_reduce_shard_ex(u, good, pre, post, FAKE, group=2, stream=0)
         assert _status(e) == "FSDP_E_RANGE"
     assert lib.fsdp_grad_reduce_shard_ex(u.handle, None, None, FAKE, None) == 1  # opts NULL
-    big = B.fsdp_unit_create(B.FSDP_FLAT, [(512 * 4,)], 512)
-    with pytest.raises(B.FsdpError) as e:
-        B.fsdp_grad_reduce_shard_ex(big, [FAKE] * 512, 1.0, 1.0, FAKE, group=256, stream=0)
-    assert _status(e) == "FSDP_E_UNSUPPORTED"
-    with pytest.raises(B.FsdpError) as e:
-        B.fsdp_grad_reduce_shard_ex(big, [FAKE] * 512, 1.0, 1.0, FAKE, accumulate=True, stream=0)
-    assert _status(e) == "FSDP_E_UNSUPPORTED"
+    with pytest.raises(ValueError):
+        B.fsdp_grad_reduce_shard_ex(u, good, 1.0, 1.0, FAKE, kernel="fast", stream=0)
+    opts = B.fsdp_reduce_opts(1.0, 1.0, 0, 0, 3, 0, None, 0)  # kernel 3 is not a kernel
+    assert lib.fsdp_grad_reduce_shard_ex(u.handle, None, ctypes.byref(opts), FAKE, None) == 2
+    # more ranks than one launch holds (128): the sums carried between launches need the
+    # caller's workspace when the output must keep its old value or a group spans launches
+    big = B.fsdp_unit_create(B.FSDP_FLAT, [(512 * 4,)], 512)  # S = 4: one slot of 64 floats
+    for group, acc, need in [(0, False, 0), (0, True, 64), (8, False, 0), (8, True, 64),
+                             (128, True, 64), (256, False, 64), (256, True, 128),
+                             (512, True, 64)]:
+        assert B.fsdp_grad_reduce_workspace(big, group=group, accumulate=acc) == need, (group, acc)
+        if need == 0:
+            continue
+        with pytest.raises(B.FsdpError) as e:  # no workspace
+            B.fsdp_grad_reduce_shard_ex(big, [FAKE] * 512, 1.0, 1.0, FAKE, group=group,
+                                        accumulate=acc, stream=0)
+        assert _status(e) == "FSDP_E_ARG"
+        for ws, ws_len, want in [(FAKE + 8, need, "FSDP_E_ALIGN"), (FAKE, need - 1, "FSDP_E_RANGE")]:
+            o = B.fsdp_reduce_opts(1.0, 1.0, group, int(acc), 0, 0, ws, ws_len)
+            table = (ctypes.c_void_p * 512)(*([FAKE] * 512))
+            st = lib.fsdp_grad_reduce_shard_ex(big.handle, ctypes.cast(table, ctypes.c_void_p),
+                                               ctypes.byref(o), FAKE, None)
+            assert B.STATUS_NAMES[st] == want, (group, acc)
+    for group in (3, 1000):
+        with pytest.raises(B.FsdpError) as e:
+            B.fsdp_grad_reduce_workspace(big, group=group)
+        assert _status(e) == "FSDP_E_RANGE"
+    # a shard that is not a multiple of 64: slots are S rounded up to 64 floats
+    odd = B.fsdp_unit_create(B.FSDP_FLAT, [(300 * 130,)], 300)  # S = 130
+    assert B.fsdp_grad_reduce_workspace(odd, group=150, accumulate=True) == 2 * 192
+    assert B.fsdp_grad_reduce_workspace(odd, group=150) == 192
+    assert B.fsdp_grad_reduce_workspace(odd, group=100, accumulate=True) == 192
     with pytest.raises(B.FsdpError) as e:
         B.fsdp_grad_reduce_shard_ex(u, [FAKE] * 7 + [FAKE + 1], 1.0, 1.0, FAKE, group=4, stream=0)
     assert _status(e) == "FSDP_E_ALIGN"

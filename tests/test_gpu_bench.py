@@ -56,10 +56,15 @@ def test_bench_json_line_on_the_tiny_unit():
     assert d["kernel_src_sha256"] == bench.kernel_src_hash()
     # the committed counter summary covers the GPT-175B unit only
     assert r["traffic"] is None and all(k["traffic"] is None for k in d["kernels"].values())
+    # the headline step runs at the rank whose flatten the sweep measured slowest
+    assert d["config"]["rank"] == pr["worst"]["flatten"]["rank"]
+    assert "slowest" in d["config"]["rank_choice"]
     c = d["cpu_baseline"]
-    assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["sample"]
+    assert c["kind"] == "oracle" and c["cores"] == bench.host_threads() and c["value"] > 0
+    assert c["sample"] and set(c["per_kernel_gbs"]) == {"flatten", "copyout", "grad_reduce", "adamw"}
+    one = c["single_core"]
+    assert one["cores"] == 1 and one["kind"] == "oracle" and one["value"] > 0
     assert "copyin_bf16_all_ranks" in d["next_rows"]
-
 
 
 def test_bench_headline_from_graph_replays_without_flush():
@@ -78,13 +83,22 @@ def test_bench_defaults_probes_and_opt_outs():
     """The rank sweep is on by default (and --no-sweep-ranks removes it); the copy and floor
     probes report what they measure; every line says how its kernel times were taken."""
     p = _run("--workload", "tiny", "--steps", "2", "--warmup", "1", "--no-cpu-baseline",
-             "--no-next", "--copy-probe", "--floor-probe")
+             "--no-next", "--copy-probe", "--floor-probe", "--contention-probe")
     assert p.returncode == 0, p.stderr[-2000:]
     d = json.loads([l for l in p.stdout.splitlines() if l.startswith("{")][0])
     assert "per_rank" in d and "timing" in d["per_rank"] and "kernel_timing" in d
     assert "next_rows" not in d
     cp = d["copy_ceiling"]
     assert set(cp) == {"library_copy", "hipMemcpyDtoD"} and all(v["GB/s"] > 0 for v in cp.values())
+    ff = d["flatten_floor"]
+    N = d["config"]["N"]
+    assert len(ff["order"]) == 5 + len({0, 1, max(0, N // 2 - 1), N - 1})
+    assert set(ff["cases"]) == set(ff["order"])
+    assert all(c["event_ms_median"] > 0 for c in ff["cases"].values())
+    ct = d["contention"]
+    for kernel in ("tiles", "sweep"):
+        assert all(ct[kernel][key] > 0 for key in ("reduce_alone_ms", "reduce_overlapped_ms",
+                                                   "gemm_overlapped_ms", "both_done_wall_ms"))
     fl = d["floor_probe"]
     assert [f["elements"] for f in fl] == [1 << lg for lg in range(20, 28)]
     assert all(f["bytes"] == 8 * f["elements"] and f["event_ms_median"] > 0 for f in fl)

@@ -12,7 +12,8 @@ import torch
 
 import oracle
 import workloads as W
-from gpu_util import assert_bf16_bits, assert_f32_bits, assert_f32_tol_then_bits, dev, to_host
+from gpu_util import (assert_bf16_bits, assert_f32_bits, assert_f32_tol_then_bits, dev,
+                      offset_view, to_host)
 from sharded_fsdp_flatten_amd import binding as B
 
 pytestmark = pytest.mark.gpu
@@ -100,6 +101,28 @@ def test_gpt175b_local_accumulation_all(unit175):
     oracle.grad_accumulate(to_host(grad), want, init=False)
     assert_f32_bits(to_host(acc), want, "175b local accumulation, all L")
     del grad, acc, want
+
+
+@pytest.mark.parametrize("init,mis_acc,mis_grad", [(True, 0, 0), (False, 0, 2), (False, 1, 1),
+                                                   (True, 3, 2)])
+def test_long_local_accumulation_variants(init, mis_acc, mis_grad):
+    """The accumulation over more than 2^18 blocks (XCD-ordered): from a zero start (init),
+    and with accumulator and gradient at element offsets (the one-element path: an
+    accumulator not 16-byte aligned; the vector path needs a 16-byte-aligned accumulator and a
+    4-byte-aligned gradient), 600 M elements, element by element against the oracle."""
+    n = 600_000_000 + 77
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(n,)], 1)
+    gen = torch.Generator(device=dev()).manual_seed(17)
+    gv, gb = offset_view(n, torch.bfloat16, mis_grad)
+    gv.copy_(torch.randn(n, device=dev(), generator=gen).mul_(1e-3).to(torch.bfloat16))
+    acc, ab = offset_view(n, torch.float32, mis_acc)
+    acc.copy_(torch.randn(n, device=dev(), generator=gen).mul_(1e-3))
+    want = to_host(acc).copy()
+    B.fsdp_grad_accumulate(u, 0, gv, acc, init)
+    _sync()
+    oracle.grad_accumulate(to_host(gv), want, init=init)
+    assert_f32_bits(to_host(acc), want, "accumulation init=%s offsets %d/%d" % (init, mis_acc, mis_grad))
+    del gv, gb, acc, ab, want
 
 
 def test_gpt175b_unscale_rank_shard(unit175):

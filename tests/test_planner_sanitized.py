@@ -12,7 +12,7 @@ import pytest
 from conftest import ROOT
 
 CSRC = os.path.join(ROOT, "sharded_fsdp_flatten_amd", "csrc")
-FLAGS = ["-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
+FLAGS = ["-std=c++17", "-O1", "-g", "-ffp-contract=off", "-fsanitize=address,undefined", "-fno-omit-frame-pointer",
          "-fno-sanitize-recover=undefined"]
 
 
