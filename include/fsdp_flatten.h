@@ -437,6 +437,28 @@ FSDP_API fsdp_status fsdp_grad_sqnorm(const fsdp_unit* unit, int32_t k, const fl
                                       double* workspace, int64_t workspace_len, double* out,
                                       void* stream);
 
+/*
+ * fsdp_grad_sqnorm for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * per-parameter sums of squares, bit for bit, with the partial sums kept in the
+ * library's own scratch instead of a caller's workspace.  The scratch is one fixed
+ * array of 262,144 doubles (2 MiB) on each GPU the library runs on, held until the
+ * process ends; its address is looked up on the first call on each device.  It keeps
+ * the last call's contents and needs no clearing: every partial sum a call reads, the
+ * same call has written first.  Calls that run at the same time on one GPU (other
+ * streams, other threads) share the array and race: order them, or give each its own
+ * workspace through fsdp_grad_sqnorm.  Allocates no device memory (it builds small host
+ * tables, as every call does).
+ *   grad : device pointer, fp32, S elements (k in [0, N)).
+ *   out  : device pointer, n_params doubles, written.
+ * Errors: FSDP_E_ARG (NULL pointers), FSDP_E_RANGE (k, or rank k's shard needs more
+ * than 262,144 partial sums: more than 2^30 elements, or runs of many parameters whose
+ * 4096-element tiles add up past that), FSDP_E_ALIGN, FSDP_E_HIP (the scratch's address
+ * cannot be obtained, or a launch failed).
+ */
+FSDP_API fsdp_status fsdp_grad_sqnorm_noalloc(const fsdp_unit* unit, int32_t k, const float* grad,
+                                              double* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

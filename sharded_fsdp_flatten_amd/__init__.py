@@ -23,6 +23,7 @@ from .binding import (  # noqa: F401
     fsdp_grad_reduce_shard_ex,
     fsdp_grad_reduce_workspace,
     fsdp_grad_sqnorm,
+    fsdp_grad_sqnorm_noalloc,
     fsdp_grad_sqnorm_workspace,
     fsdp_grad_unscale,
     fsdp_last_error,

@@ -124,6 +124,8 @@ def load() -> ctypes.CDLL:
     lib.fsdp_grad_unscale.restype = st
     lib.fsdp_grad_sqnorm_workspace.argtypes = [_vp, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]
     lib.fsdp_grad_sqnorm_workspace.restype = st
+    lib.fsdp_grad_sqnorm_noalloc.argtypes = [_vp, ctypes.c_int32, _vp, _vp, _vp]
+    lib.fsdp_grad_sqnorm_noalloc.restype = st
     lib.fsdp_grad_sqnorm.argtypes = [_vp, ctypes.c_int32, _vp, _vp, ctypes.c_int64, _vp, _vp]
     lib.fsdp_grad_sqnorm.restype = st
     _lib = lib
@@ -450,10 +452,20 @@ def fsdp_grad_sqnorm(unit: Unit, k: int, grad, out, workspace, stream=None) -> N
                                    _addr(out, _F64) or None, _stream(stream, grad)))
 
 
+def fsdp_grad_sqnorm_noalloc(unit: Unit, k: int, grad, out, stream=None) -> None:
+    """fsdp_grad_sqnorm with the partial sums in the library's own per-GPU scratch (no
+    workspace; calls that overlap on one GPU race)."""
+    _need(grad, unit.S, "grad")
+    _need(out, len(unit.shapes), "out")
+    _check(load().fsdp_grad_sqnorm_noalloc(unit.handle, k, _addr(grad, _F32) or None,
+                                           _addr(out, _F64) or None, _stream(stream, grad)))
+
+
 ABI_FUNCTIONS = ["fsdp_abi_version", "fsdp_last_error", "fsdp_status_string", "fsdp_unit_create",
                  "fsdp_unit_destroy", "fsdp_unit_info", "fsdp_unit_param_offset", "fsdp_unit_recv_pitch",
                  "fsdp_flatten_shard", "fsdp_unflatten_copyout", "fsdp_grad_reduce_shard",
                  "fsdp_adam_shard", "fsdp_cast_to_bf16", "fsdp_unflatten_copyout_bf16",
                  "fsdp_flatten_shard_bf16", "fsdp_grad_reduce_shard_ex", "fsdp_grad_reduce_workspace",
                  "fsdp_grad_accumulate",
-                 "fsdp_grad_unscale", "fsdp_grad_sqnorm_workspace", "fsdp_grad_sqnorm"]
+                 "fsdp_grad_unscale", "fsdp_grad_sqnorm_workspace", "fsdp_grad_sqnorm",
+                 "fsdp_grad_sqnorm_noalloc"]

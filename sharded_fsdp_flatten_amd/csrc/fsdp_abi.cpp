@@ -507,4 +507,32 @@ fsdp_status fsdp_grad_sqnorm(const fsdp_unit* unit, int32_t k, const float* grad
     });
 }
 
+fsdp_status fsdp_grad_sqnorm_noalloc(const fsdp_unit* unit, int32_t k, const float* grad,
+                                     double* out, void* stream) {
+    return guarded("fsdp_grad_sqnorm_noalloc", [&]() -> fsdp_status {
+        if (!unit) return fail(FSDP_E_ARG, "unit is NULL");
+        const fsdp::UnitPlan& u = unit->plan;
+        if (k < 0 || k >= u.N) return fail(FSDP_E_RANGE, "k must be in [0, N)");
+        std::vector<fsdp::ParamRun> runs;
+        fsdp::plan_param_runs(u, k, &runs);
+        const int64_t need = fsdp::sqnorm_tiles(runs);
+        fsdp_status s;
+        if ((s = check_buf(grad, u.S, sizeof(float), "grad")) != FSDP_OK) return s;
+        if ((s = check_buf(out, static_cast<int64_t>(runs.size()), sizeof(double), "out")) != FSDP_OK)
+            return s;
+        if (need > fsdp::sqnorm_scratch_doubles())
+            return fail(FSDP_E_RANGE, "rank " + std::to_string(k) + " needs " + std::to_string(need) +
+                                          " partial sums; the library's scratch holds " +
+                                          std::to_string(fsdp::sqnorm_scratch_doubles()) +
+                                          " (use fsdp_grad_sqnorm with a workspace)");
+        if (runs.empty()) return ok();
+        double* partial = nullptr;
+        hipError_t e = fsdp::sqnorm_scratch(&partial);
+        if (e != hipSuccess) return hip_fail(e, "fsdp_grad_sqnorm_noalloc scratch lookup");
+        e = fsdp::launch_grad_sqnorm(grad, runs, partial, out, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "fsdp_grad_sqnorm_noalloc launch");
+        return ok();
+    });
+}
+
 }  // extern "C"

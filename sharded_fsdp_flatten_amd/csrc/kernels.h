@@ -61,4 +61,11 @@ int64_t sqnorm_tiles(const std::vector<ParamRun>& runs);
 hipError_t launch_grad_sqnorm(const float* g, const std::vector<ParamRun>& runs, double* partial,
                               double* out, hipStream_t stream);
 
+// The library's own scratch for the partial sums of launch_grad_sqnorm, for callers that
+// cannot allocate: sqnorm_scratch_doubles() doubles per GPU; *out receives the current
+// device's copy (looked up on the first call on each device).  Calls that use it at the
+// same time on one GPU race.
+int64_t sqnorm_scratch_doubles();
+hipError_t sqnorm_scratch(double** out);
+
 }  // namespace fsdp

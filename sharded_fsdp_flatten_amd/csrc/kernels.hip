@@ -1441,6 +1441,35 @@ hipError_t launch_grad_unscale(float* g, int64_t len, float inv_scale, float* fo
     return hipGetLastError();
 }
 
+// Scratch for callers that cannot allocate device memory: the binary64 partial sums of the
+// sums of squares, one fixed array per GPU (a global of this code object, so every device the
+// library runs on holds its own copy until the process ends).  Only its device address is
+// used on the host; the name here is a host-side stand-in.
+constexpr int64_t kScratchDoubles = int64_t{1} << 18;  // 2 MiB
+static __device__ __align__(256) double scratch[kScratchDoubles];
+
+int64_t sqnorm_scratch_doubles() { return kScratchDoubles; }
+
+hipError_t sqnorm_scratch(double** out) {
+    // the address of the current device's copy, looked up on the first call on that device
+    static std::atomic<double*> addr[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    double* p = addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        void* q = nullptr;
+        e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (q == nullptr) return hipErrorInvalidSymbol;
+        p = static_cast<double*>(q);
+        addr[dev].store(p, std::memory_order_release);  // racing first calls store the same address
+    }
+    *out = p;
+    return hipSuccess;
+}
+
 int64_t sqnorm_tiles(const std::vector<ParamRun>& runs) {
     int64_t n = 0;
     for (const ParamRun& r : runs) n += (r.n + kSqTile - 1) / kSqTile;

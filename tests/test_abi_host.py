@@ -471,6 +471,19 @@ def test_unscale_and_sqnorm_errors(B):
     assert lib.fsdp_grad_unscale(e.handle, 0, None, 0.5, None, None) == 0
     assert lib.fsdp_grad_sqnorm_workspace(e.handle, 0, ctypes.byref(n)) == 0 and n.value == 0
     assert lib.fsdp_grad_sqnorm(e.handle, 0, None, None, 0, None, None) == 0
+    # the allocation-free variant validates the same way, and refuses shards whose partial
+    # sums do not fit its 262,144-double scratch, before any HIP call
+    assert lib.fsdp_grad_sqnorm_noalloc(None, 0, g, o, None) == 1
+    assert lib.fsdp_grad_sqnorm_noalloc(u.handle, 2, g, o, None) == 2
+    assert lib.fsdp_grad_sqnorm_noalloc(u.handle, 1, None, o, None) == 1
+    assert lib.fsdp_grad_sqnorm_noalloc(u.handle, 1, g, None, None) == 1
+    assert lib.fsdp_grad_sqnorm_noalloc(u.handle, 1, g, o + 4, None) == 3
+    assert lib.fsdp_grad_sqnorm_noalloc(e.handle, 0, None, None, None) == 0
+    big = B.fsdp_unit_create(B.FSDP_FLAT, [((1 << 18) * 4096 + 1,)], 1)
+    assert lib.fsdp_grad_sqnorm_workspace(big.handle, 0, ctypes.byref(n)) == 0
+    assert n.value == (1 << 18) + 1
+    assert lib.fsdp_grad_sqnorm_noalloc(big.handle, 0, g, o, None) == 2
+    assert "holds 262144" in B.fsdp_last_error()
 
 
 def test_binding_refuses_host_tensors(B):
