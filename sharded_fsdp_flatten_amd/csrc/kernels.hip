@@ -19,9 +19,9 @@
 //     the bf16 copies.  The host planner turns the layout into a short table of
 //     (src, dst, length[, block stride]) segments passed in the kernel argument
 //     block; each workgroup takes one tile of one segment (the tile -> segment
-//     lookup is wave-uniform, on scalar registers: a count over tables of up to 4
-//     segments, loaded at once, a binary search over larger ones), so no lane
-//     ever searches and every tile is a straight streaming copy.  Launches of
+//     lookup is wave-uniform, on scalar registers: the segment with the most tiles
+//     is loaded with the table's header, the others found by a binary search), so
+//     no lane ever searches and every tile is a straight streaming copy.  Launches of
 //     2^18 tiles or more hand each XCD runs of 256 consecutive tiles.  When source
 //     and destination are not 16-byte co-aligned, a scalar head aligns the
 //     destination and the source is read in place with dword-aligned 16-byte
@@ -91,6 +91,14 @@ constexpr uint32_t kXcdMinTiles = 1u << 18;
 constexpr uint32_t kXcdChunk = 256u;
 constexpr int kReduceThreads = 64;   // reduction tile kernel: one wave per 512-output tile
 constexpr int kReduceAhead = 8;      // ranks loaded before their adds in the tile kernel
+// The tile kernel needs few registers (47 VGPRs), so up to 8 of its waves per SIMD would be
+// resident, and more contribution rows in flight at once read more slowly.  Each workgroup
+// reserves this much LDS it does not use, which caps residency at 29 workgroups per CU (7.25
+// waves per SIMD).  rocprofv3, alternating processes on one box: the T5 block's 8-way reduction
+// 80.3-80.4 against 84.7-85.2 us uncapped (6, 5, 4 waves per SIMD: 81.1-81.8, 85.3-85.5,
+// 90.1 us), the GPT-175B hybrid accumulating reduction on this kernel 570.7-572.1 against
+// 594.5-595.9 us; the GPT-2-L block's 10.5-10.6 us either way.
+constexpr unsigned kReduceLdsCap = 5632;
 constexpr int kSweepMinRanks = 32;   // the flat reduction sweeps ranks row-major from this many
 constexpr int kSweepMinTiles = 12288;  // ... and from this many whole 512-output tiles on
 constexpr int kSweepV = 16;          // whole tiles a flat sweep wave holds (8/12/16: 6.23/6.36/6.53)
@@ -253,13 +261,15 @@ struct DevSeg {
     int64_t src_stride, dst_stride;
 };
 // A launch's segments, passed by value in the kernel-argument block: a table of kCap entries,
-// the smallest of 1, 4, 16 and kMaxSegs that holds the launch's segments.
+// the smallest of 1, 4, 16 and kMaxSegs that holds the launch's segments, and a copy of the
+// segment with the most tiles next to the header.
 template <int kCap>
 struct SegTable {
     uint32_t ntiles;
     uint32_t nseg;
-    uint32_t xcd_runs;  // tiles in XCD-chunked order (xcd_chunked)
-    uint32_t unused;
+    uint32_t xcd_runs;   // tiles in XCD-chunked order (xcd_chunked)
+    uint32_t hot_tiles;  // tiles of `hot`
+    DevSeg hot;          // the segment with the most tiles (unused in one-segment tables)
     DevSeg seg[kCap];
 };
 static_assert(sizeof(SegTable<kMaxSegs>) <= 4096, "segment table must fit one kernel argument block");
@@ -387,48 +397,39 @@ __device__ __forceinline__ void copy_tile(const DevSeg& sg, uint32_t local, SrcT
         tile_aligned<SrcT, DstT>(s, d, n);
 }
 
-// One tile per workgroup (grid = number of tiles).  The tile's segment is found from the
-// table with wave-uniform scalar loads, and a workgroup's first vector load waits for them.
-// Tables of up to 4 segments are read at the start with one wait -- the empty asm statements
-// pin the loads there, where the compiler would issue each just before its first use, after
-// the previous one's wait -- and the segment is found by counting first tiles; one-segment
-// tables load the segment's fields with them.  On the GPT-175B block's rank flatten (rocprofv3,
-// cold cache, two rounds on one box) a one-segment shard took 18.72-18.84 against 19.04-19.28
-// us with the search, a two-segment one 19.24-19.28 against 19.64-19.76.  Larger tables
-// search: counting 16 entries made the five-segment rank 0 take 21.0-21.5 us against 20.2-20.3.
+// One tile per workgroup (grid = number of tiles).  The tile's segment comes from the table
+// through wave-uniform scalar loads, and a workgroup's first vector load waits for them, so
+// the kernel reads everything most tiles need in one round trip: the empty asm statements pin
+// the loads at the start, where the compiler would issue each just before its first use,
+// after the previous one's wait.  A one-segment table loads that segment with the header; a
+// larger one loads the copy of its segment with the most tiles, and only the tiles outside it
+// search the table.  GPT-175B block, rank flatten, rocprofv3 durations (cold cache, two rounds
+// on one box): one segment 18.72-18.84 us against 19.04-19.28 with the search for every tile;
+// rank 0's five segments (four LayerNorm tensors of 12 tiles before the big one) 19.20 against
+// 20.16-20.40.
 template <typename SrcT, typename DstT, bool kGeneral, int kCap>
 __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable<kCap> t) {
     constexpr int kTile = tile_elems<SrcT, DstT>();
     __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral && sizeof(SrcT) == 2 ? kTile + 16 : 8];
     const uint32_t ntiles = t.ntiles, nseg = t.nseg, xcdr = t.xcd_runs;
-    uint32_t lo = 0;
-    if constexpr (kCap <= 4) {
-        uint32_t t0[kCap];
-#pragma unroll
-        for (int i = 0; i < kCap; ++i) t0[i] = t.seg[i].tile0;
-        asm volatile("" ::"s"(ntiles), "s"(nseg), "s"(xcdr));
-#pragma unroll
-        for (int i = 0; i < kCap; ++i) asm volatile("" ::"s"(t0[i]));
-        if constexpr (kCap == 1) {
-            const DevSeg& z = t.seg[0];
-            asm volatile("" ::"s"(z.src), "s"(z.dst), "s"(z.blk_n), "s"(z.last_n), "s"(z.nblk),
-                         "s"(z.tiles_per_blk), "s"(z.src_stride), "s"(z.dst_stride));
-        }
-        const uint32_t tile = xcdr ? xcd_chunked<kXcdChunk>(blockIdx.x, ntiles) : blockIdx.x;
-#pragma unroll
-        for (int i = 1; i < kCap; ++i) lo += (static_cast<uint32_t>(i) < nseg && t0[i] <= tile) ? 1u : 0u;
-        const DevSeg& sg = t.seg[lo];
-        copy_tile<SrcT, DstT, kGeneral>(sg, tile - sg.tile0, lds);
-    } else {
-        const uint32_t tile = xcdr ? xcd_chunked<kXcdChunk>(blockIdx.x, ntiles) : blockIdx.x;
-        uint32_t hi = nseg - 1;
-        while (lo < hi) {
-            const uint32_t mid = (lo + hi + 1) >> 1;
-            if (t.seg[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
-        }
-        const DevSeg& sg = t.seg[lo];
-        copy_tile<SrcT, DstT, kGeneral>(sg, tile - sg.tile0, lds);
+    const DevSeg& z = kCap == 1 ? t.seg[0] : t.hot;
+    const uint32_t hot_tiles = kCap == 1 ? ntiles : t.hot_tiles;
+    asm volatile("" ::"s"(ntiles), "s"(nseg), "s"(xcdr), "s"(hot_tiles), "s"(z.src), "s"(z.dst),
+                 "s"(z.blk_n), "s"(z.last_n), "s"(z.nblk), "s"(z.tiles_per_blk), "s"(z.tile0),
+                 "s"(z.src_stride), "s"(z.dst_stride));
+    const uint32_t tile = xcdr ? xcd_chunked<kXcdChunk>(blockIdx.x, ntiles) : blockIdx.x;
+    if (kCap == 1 || tile - z.tile0 < hot_tiles) {
+        copy_tile<SrcT, DstT, kGeneral>(z, tile - z.tile0, lds);
+        return;
     }
+    // wave-uniform binary search of the segment holding this tile
+    uint32_t lo = 0, hi = nseg - 1;
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (t.seg[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
+    }
+    const DevSeg& sg = t.seg[lo];
+    copy_tile<SrcT, DstT, kGeneral>(sg, tile - sg.tile0, lds);
 }
 
 // ---------------------------------------------------------------------------
@@ -1033,7 +1034,16 @@ void launch_table(const SegTable<kMaxSegs>& full, bool general, uint64_t tiles, 
     t.ntiles = full.ntiles;
     t.nseg = full.nseg;
     t.xcd_runs = full.xcd_runs;
-    for (uint32_t i = 0; i < full.nseg; ++i) t.seg[i] = full.seg[i];
+    uint32_t hot = 0;
+    for (uint32_t i = 0; i < full.nseg; ++i) {
+        t.seg[i] = full.seg[i];
+        const uint32_t end = i + 1 < full.nseg ? full.seg[i + 1].tile0 : full.ntiles;
+        if (end - full.seg[i].tile0 > t.hot_tiles) {
+            t.hot_tiles = end - full.seg[i].tile0;
+            hot = i;
+        }
+    }
+    t.hot = full.seg[hot];
     if (general)
         hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, true, kCap>), grid_of(tiles), dim3(kThreads), 0,
                            stream, t);
@@ -1094,12 +1104,13 @@ template <int kPre, int kLd>
 void launch_reduce_mode(const ReduceArgs& a, bool hybrid, bool accum, dim3 grid,
                         hipStream_t stream) {
     const dim3 block(kReduceThreads);
+    const unsigned lds = kReduceLdsCap;  // residency cap (unused LDS)
     if (hybrid) {
-        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kLd, true, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((reduce_kernel<kPre, kLd, true, false>), grid, block, 0, stream, a);
+        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kLd, true, true>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((reduce_kernel<kPre, kLd, true, false>), grid, block, lds, stream, a);
     } else {
-        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kLd, false, true>), grid, block, 0, stream, a);
-        else hipLaunchKernelGGL((reduce_kernel<kPre, kLd, false, false>), grid, block, 0, stream, a);
+        if (accum) hipLaunchKernelGGL((reduce_kernel<kPre, kLd, false, true>), grid, block, lds, stream, a);
+        else hipLaunchKernelGGL((reduce_kernel<kPre, kLd, false, false>), grid, block, lds, stream, a);
     }
 }
 
