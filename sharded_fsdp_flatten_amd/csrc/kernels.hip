@@ -32,10 +32,11 @@
 //     whole tiles swap halves across lanes so each store writes 1 KiB; the tile
 //     the output's end cuts runs first, its last len % 8 outputs one per lane.
 //     From 32 ranks and 12,288 whole tiles on, a row-major sweep instead: each
-//     wave holds 16 tiles' sums (8 with hybrid groups, whose sums it also holds)
-//     and walks the ranks in order, the grid sized to be resident at once (each
-//     XCD one contiguous run of waves), so HBM serves a few contribution rows at
-//     a time.  More ranks than one launch holds (128) take several launches that
+//     wave holds 16 tiles' sums with one rank in flight, or 8 tiles' group sums
+//     and totals with two ranks in flight (hybrid groups; the flat sum as one
+//     group where that shape's runs are long), and walks the ranks in order, the
+//     grid sized to be resident at once (each XCD one contiguous run of waves),
+//     so HBM serves a few contribution rows at a time.  More ranks than one launch holds (128) take several launches that
 //     carry their exact running sums through the output or a caller's workspace.
 //   - adamw: elementwise over 8 elements per lane, 128-bit loads and stores.
 //     Its state is read and written back in place: plain loads measure faster
@@ -101,8 +102,16 @@ constexpr int kReduceAhead = 8;      // ranks loaded before their adds in the ti
 constexpr unsigned kReduceLdsCap = 5632;
 constexpr int kSweepMinRanks = 32;   // the flat reduction sweeps ranks row-major from this many
 constexpr int kSweepMinTiles = 12288;  // ... and from this many whole 512-output tiles on
-constexpr int kSweepV = 16;          // whole tiles a flat sweep wave holds (8/12/16: 6.23/6.36/6.53)
-constexpr int kHybridSweepV = 8;     // and a hybrid one (it also holds its group's sums)
+// The sweep has two shapes.  The wide one (flat sums only) holds 16 tiles per wave and one
+// rank in flight (8/12/16 tiles: 6.23/6.36/6.53 TB/s); the grouped one holds 8 tiles' group
+// sums and totals and two ranks in flight: the hybrid reduction, and the flat one as a single
+// group where every run of the grouped shape holds at least kGroupSweepMinRunTiles tiles (its
+// waves then fill the device; with fewer it is the slower, see launch_reduce_sweep).
+constexpr int kSweepV = 16;
+constexpr int kSweepAhead = 1;
+constexpr int kGroupSweepV = 8;
+constexpr int kGroupSweepAhead = 2;
+constexpr int64_t kGroupSweepMinRunTiles = 12288;
 constexpr int kUnscaleVpl = 4;       // 4-element vectors per lane in the gradient unscale
 // The in-place local accumulation over all L of the GPT-175B unit (885k blocks of 2048) takes
 // runs of 128 blocks per XCD: 6.38-6.40 TB/s, against 5.87-5.88 in dispatch order and runs of
@@ -753,15 +762,15 @@ __global__ __launch_bounds__(kReduceThreads) void reduce_kernel(ReduceArgs a) {
 // its 512 outputs, so the waves in flight read from all ranks' rows at once (128
 // contribution rows on a 128-rank shard), and HBM serves that many scattered streams
 // more slowly than a few (read-only: 6.5 against 7.0 TB/s).  Here each wave owns kV
-// consecutive whole tiles (8 kV sums per lane) and walks the ranks in order, loading
-// rank r + 1's kV vectors while it adds rank r's; the host sizes the grid so that
-// every wave is resident at once, so the waves move through the ranks together and
-// HBM serves a few rows at a time.  Per output the operations and their order are
-// those of the tile path (whole-dword contributions), so the results are identical.
-// Hybrid groups keep a second set of kV x 8 sums per lane (the group's), folded into
-// the total after each group's last rank; with the total's registers that allows
-// fewer tiles per wave.  Block layout of a launch: the tile the output's end cuts (if
-// any), then n_single whole tiles that take the tile path, then the sweep waves.
+// consecutive whole tiles (8 kV sums per lane) and walks the ranks in order, with the
+// next kA ranks' kV vectors in flight; the host sizes the grid so that every wave is
+// resident at once, so the waves move through the ranks together and HBM serves a few
+// rows at a time.  Per output the operations and their order are those of the tile path
+// (whole-dword contributions), so the results are identical.  The grouped shape
+// (kHybrid) keeps a second set of kV x 8 sums per lane (the group's), folded into the
+// total after each group's last rank.  Block layout of a launch: the tile the output's
+// end cuts (if any), then n_single whole tiles that take the tile path, then the sweep
+// waves.
 struct SweepArgs {
     ReduceArgs r;
     int64_t t_first;   // first whole tile (512 outputs) of this launch
@@ -802,23 +811,63 @@ __device__ __forceinline__ void sweep_wave(const ReduceArgs& a, int64_t t0) {
         }
     }
     int pos = a.pos0;
-    u4 x[kV];  // rank r's vectors
-    const uint16_t* c0 = a.c[0] + base;
+    // kA ranks' vectors in flight: slot q holds rank r + q while rank r is added.  With
+    // kA = 2 the reload is conditional (the last ranks have none), and the compiler loads
+    // into fresh registers, then waits for those loads before the adds of the rank in hand:
+    // each wave streams a burst, then computes.  That measured faster than the forms that
+    // overlap the two (the grouped 128-way reduction of the GPT-175B shard, rocprofv3:
+    // 535-541 us against 557-577 us for explicit overlapped, copy-and-wait and
+    // unconditional-reload versions).
+    constexpr int kA = kHybrid ? kGroupSweepAhead : kSweepAhead;
+    u4 x[kA][kV];
 #pragma unroll
-    for (int v = 0; v < kV; ++v) x[v] = ldu4w(c0 + off + kTile * v);
-    for (int r = 0; r + 1 < a.nc; ++r) {
-        const uint16_t* cn = a.c[r + 1] + base;
+    for (int q = 0; q < kA; ++q) {
+        if (q >= a.nc) break;
+        const uint16_t* cq = a.c[q] + base;
+#pragma unroll
+        for (int v = 0; v < kV; ++v) x[q][v] = ldu4w(cq + off + kTile * v);
+    }
+    int r = 0;
+    for (; r + kA < a.nc; r += kA) {
+#pragma unroll
+        for (int q = 0; q < kA; ++q) {
+            // rank r + q is added, and its slot reloaded with rank r + q + kA (if any)
+            const bool more = kA == 1 || r + q + kA < a.nc;  // kA == 1: the loop bound
+            const uint16_t* cn = a.c[more ? r + q + kA : 0] + base;
+#pragma unroll
+            for (int v = 0; v < kV; ++v) {
+                // one vector at a time, its adds before its reload: no second copy of any
+                // vector is live
+                if constexpr (kHybrid) add8<kPre>(s[v], x[q][v], a);
+                else add8<kPre>(acc[v], x[q][v], a);
+                if (more) x[q][v] = ldu4w(cn + off + kTile * v);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            if constexpr (kHybrid) {
+                // a group that ends with this rank is folded into the total (wave-uniform)
+                if (++pos == a.group) {
+#pragma unroll
+                    for (int v = 0; v < kV; ++v)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            acc[v][e] = acc[v][e] + s[v][e];
+                            s[v][e] = -0.0f;
+                        }
+                    pos = 0;
+                }
+            }
+        }
+    }
+    // the last ranks r .. nc - 1, already loaded into slots 0 .. nc - 1 - r
+#pragma unroll
+    for (int q = 0; q < kA; ++q) {
+        if (r + q >= a.nc) break;
 #pragma unroll
         for (int v = 0; v < kV; ++v) {
-            // one vector at a time, its adds before its reload: no second copy of any
-            // vector is live
-            if constexpr (kHybrid) add8<kPre>(s[v], x[v], a);
-            else add8<kPre>(acc[v], x[v], a);
-            x[v] = ldu4w(cn + off + kTile * v);
-            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (kHybrid) add8<kPre>(s[v], x[q][v], a);
+            else add8<kPre>(acc[v], x[q][v], a);
         }
         if constexpr (kHybrid) {
-            // a group that ends with rank r is folded into the total (wave-uniform)
             if (++pos == a.group) {
 #pragma unroll
                 for (int v = 0; v < kV; ++v)
@@ -829,19 +878,6 @@ __device__ __forceinline__ void sweep_wave(const ReduceArgs& a, int64_t t0) {
                     }
                 pos = 0;
             }
-        }
-    }
-#pragma unroll
-    for (int v = 0; v < kV; ++v) {
-        if constexpr (kHybrid) add8<kPre>(s[v], x[v], a);
-        else add8<kPre>(acc[v], x[v], a);
-    }
-    if constexpr (kHybrid) {
-        if (++pos == a.group) {
-#pragma unroll
-            for (int v = 0; v < kV; ++v)
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[v][e] = acc[v][e] + s[v][e];
         }
     }
 #pragma unroll
@@ -1258,7 +1294,7 @@ hipError_t launch_segcopy(const std::vector<CopySeg>& segs, Pipe pipe, hipStream
 constexpr int kMaxDevices = 64;
 template <int kPre, bool kAccum, bool kHybrid>
 int64_t sweep_capacity() {
-    constexpr int kV = kHybrid ? kHybridSweepV : kSweepV;
+    constexpr int kV = kHybrid ? kGroupSweepV : kSweepV;
     static std::atomic<int64_t> cap[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
@@ -1282,7 +1318,7 @@ int64_t sweep_capacity() {
 // or the occupancy is unknown.
 template <int kPre, bool kAccum, bool kHybrid>
 bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
-    constexpr int kV = kHybrid ? kHybridSweepV : kSweepV;
+    constexpr int kV = kHybrid ? kGroupSweepV : kSweepV;
     constexpr int64_t kTile = 512;
     std::vector<SweepRun> runs;
     if (!plan_sweep_runs(a.len / kTile, a.len % kTile != 0, kV,
@@ -1302,11 +1338,31 @@ bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
     return true;
 }
 
+// The flat sum takes the grouped shape where its runs are long, and runs there as one group
+// that spans every rank: the group's sum is the running sum, carried in and out where the
+// flat path carries its total, and the last launch ends the group, whose sum then becomes the
+// total as it is (no total came before it).  Per output the operations and their order are
+// the flat ones.  rocprofv3, cold cache, the grouped against the wide shape in TB/s: 128 ranks
+// over 14.2 M outputs (two runs of 13,825 tiles) 6.66 against 6.46, over 26.2 M (four runs)
+// 6.54 against 6.28; 64 ranks 6.53 / 6.35 and 6.35 / 6.19; 32 ranks 6.15 / 6.17 and 5.99 /
+// 5.97; but over 8.4 M outputs, two runs of 8,192 tiles, 5.36 against 6.55 at 128 ranks.
 template <int kPre>
 bool launch_reduce_sweep(const ReduceArgs& a, bool hybrid, bool accum, hipStream_t stream,
                          hipError_t* err) {
     if (hybrid)
         return accum ? try_sweep<kPre, true, true>(a, stream, err) : try_sweep<kPre, false, true>(a, stream, err);
+    std::vector<SweepRun> runs;
+    const int64_t cap = accum ? sweep_capacity<kPre, true, true>() : sweep_capacity<kPre, false, true>();
+    if (plan_sweep_runs(a.len / 512, a.len % 512 != 0, kGroupSweepV, cap, &runs) &&
+        runs.back().n_tiles >= kGroupSweepMinRunTiles) {  // the last run is the shortest
+        ReduceArgs g = a;
+        g.flags = (a.flags & kLast) | ((a.flags & kTIn) ? kSIn : 0u) | ((a.flags & kTOut) ? kSOut : 0u);
+        g.carry_s = a.carry_t;
+        g.carry_t = nullptr;
+        g.pos0 = (a.flags & kTIn) ? 1 : 0;  // a carried-in sum is continued, not restarted
+        g.group = g.pos0 + a.nc + ((a.flags & kLast) ? 0 : 1);
+        return accum ? try_sweep<kPre, true, true>(g, stream, err) : try_sweep<kPre, false, true>(g, stream, err);
+    }
     return accum ? try_sweep<kPre, true, false>(a, stream, err) : try_sweep<kPre, false, false>(a, stream, err);
 }
 

@@ -44,7 +44,9 @@ def _reduce(u, c, pre, post, out=None, accumulate=False):
         out = torch.full((S,), float("nan"), device=dev())
     rows = [c[r] for r in range(c.shape[0])]
     if accumulate:
-        B.fsdp_grad_reduce_shard_ex(u, rows, pre, post, out, accumulate=True)
+        need = B.fsdp_grad_reduce_workspace(u, accumulate=True)
+        ws = torch.full((need,), float("nan"), device=dev()) if need else None
+        B.fsdp_grad_reduce_shard_ex(u, rows, pre, post, out, accumulate=True, workspace=ws)
     else:
         B.fsdp_grad_reduce_shard(u, rows, pre, post, out)
     torch.cuda.synchronize()
@@ -58,6 +60,8 @@ def _reduce(u, c, pre, post, out=None, accumulate=False):
     (64, 12345, 300, 1.0, 64.0),            # 9 single tiles, no pre-divide
     (33, 12290, 511, -8.0, 4.125),          # negative power-of-two pre, non-power post
     (128, 27650, 224, 8.0, 16.0),           # the GPT-175B shard length at 128 ranks
+    (128, 20000, 77, 8.0, 16.0),            # runs of 10,000 tiles: the wide shape
+    (32, 24000, 0, 2.0, 16.0),              # runs of 12,000 tiles: the wide shape
 ])
 def test_sweep_reduce(N, tiles, tail, pre, post):
     S = tiles * TILE + tail
@@ -80,11 +84,36 @@ def test_sweep_split_into_runs():
                              "sweep in runs S=%d" % S)
 
 
-@pytest.mark.parametrize("N", [160, 130, 300])
-def test_sweep_chained_over_more_than_128_ranks(N):
+@pytest.mark.parametrize("group,tiles,tail", [
+    (0, 150001, 261),   # flat, 16 tiles per wave: five runs at 2,048 resident workgroups
+    (8, 70001, 13),     # hybrid groups of 8, accumulating, 8 tiles per wave: five runs
+])
+def test_sweep_runs_over_several_launches(group, tiles, tail):
+    """Five runs (five launches), the last with the cut tile; a hybrid wave's group sums
+    start afresh in every run."""
+    N, S = 32, tiles * TILE + tail
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    c, ch = _contribs(N, S, step=9)
+    old = W.host_normal(S, 1e-3, seed=23)
+    out = to_dev(old)
+    B.fsdp_grad_reduce_shard_ex(u, [c[r] for r in range(N)], 2.0, 16.0, out, group=group,
+                                accumulate=group > 0, kernel="sweep")
+    torch.cuda.synchronize()
+    if group:
+        want = oracle.grad_reduce_ex(list(ch), 2.0, 16.0, group=group, out=old)
+    else:
+        want = oracle.grad_reduce(list(ch), 2.0, 16.0)
+    assert_f32_tol_then_bits(to_host(out), want, "sweep runs group=%d S=%d" % (group, S))
+
+
+@pytest.mark.parametrize("N,tiles", [(160, MIN_TILES), (130, MIN_TILES), (300, MIN_TILES),
+                                     (160, 20000)])
+def test_sweep_chained_over_more_than_128_ranks(N, tiles):
     """160 = 128 + 32 (two sweeps), 130 = 128 + 2 (a sweep, then the tile kernel continues
-    from the partial sums), 300 = 128 + 128 + 44 (a middle launch neither first nor last)."""
-    S = MIN_TILES * TILE + 1000
+    from the partial sums), 300 = 128 + 128 + 44 (a middle launch neither first nor last);
+    12,289 whole tiles take the grouped shape (the flat sum as one group whose running sum
+    crosses the launches), 20,000 the wide one."""
+    S = tiles * TILE + 1000
     u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
     c, ch = _contribs(N, S, step=5)
     pre = 8.0 if N != 300 else 3.0
@@ -93,8 +122,12 @@ def test_sweep_chained_over_more_than_128_ranks(N):
                              "chained N=%d" % N)
 
 
-def test_sweep_accumulate():
-    N, S = 64, (MIN_TILES + 5) * TILE + 33
+@pytest.mark.parametrize("N,tiles", [(64, MIN_TILES + 5), (64, 20000), (160, MIN_TILES + 5)])
+def test_sweep_accumulate(N, tiles):
+    """Accumulation on the grouped shape, on the wide one, and over two launches (160 ranks:
+    the running sum crosses them in the caller's workspace, the old value stays in the
+    output until the last)."""
+    S = tiles * TILE + 33
     u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
     old = W.host_normal(S, 1e-3, seed=21)
     acc = to_dev(old)
@@ -102,7 +135,7 @@ def test_sweep_accumulate():
         c, ch = _contribs(N, S, step=30 + t)
         _reduce(u, c, pre, post, out=acc, accumulate=True)
         oracle.grad_reduce_ex(list(ch), pre, post, out=old)
-        assert_f32_tol_then_bits(to_host(acc), old, "sweep accumulate step %d" % t)
+        assert_f32_tol_then_bits(to_host(acc), old, "sweep accumulate N=%d S=%d step %d" % (N, S, t))
         del c, ch
 
 
