@@ -102,15 +102,15 @@ constexpr int kReduceAhead = 8;      // ranks loaded before their adds in the ti
 constexpr unsigned kReduceLdsCap = 5632;
 constexpr int kSweepMinRanks = 32;   // the flat reduction sweeps ranks row-major from this many
 constexpr int kSweepMinTiles = 12288;  // ... and from this many whole 512-output tiles on
-// The sweep has two shapes.  The wide one (flat sums only) holds 16 tiles per wave and one
-// rank in flight (8/12/16 tiles: 6.23/6.36/6.53 TB/s); the grouped one holds 8 tiles' group
-// sums and totals and two ranks in flight: the hybrid reduction, and the flat one as a single
-// group where every run of the grouped shape holds at least kGroupSweepMinRunTiles tiles (its
-// waves then fill the device; with fewer it is the slower, see launch_reduce_sweep).
+// Shapes of the sweep.  The wide one (flat sums) holds 16 tiles' sums per wave and one rank
+// in flight (8/12/16 tiles: 6.23/6.36/6.53 TB/s).  The grouped ones hold 8 tiles' group sums
+// and totals, with two ranks in flight (232 VGPRs, 2 waves per SIMD) where every run of that
+// shape holds at least kGroupSweepMinRunTiles tiles, its waves then filling the device (the
+// flat sum takes it too, as one group), else one (168 VGPRs, 3 waves per SIMD; the hybrid sum
+// only).  Measurements in launch_reduce_sweep.
 constexpr int kSweepV = 16;
-constexpr int kSweepAhead = 1;
 constexpr int kGroupSweepV = 8;
-constexpr int kGroupSweepAhead = 2;
+constexpr int kGroupSweepLongAhead = 2;
 constexpr int64_t kGroupSweepMinRunTiles = 12288;
 constexpr int kUnscaleVpl = 4;       // 4-element vectors per lane in the gradient unscale
 // The in-place local accumulation over all L of the GPT-175B unit (885k blocks of 2048) takes
@@ -778,7 +778,7 @@ struct SweepArgs {
     int32_t n_single;  // then this many blocks reduce one whole tile each
 };
 
-template <int kPre, bool kAccum, bool kHybrid, int kV>
+template <int kPre, bool kAccum, bool kHybrid, int kV, int kA>
 __device__ __forceinline__ void sweep_wave(const ReduceArgs& a, int64_t t0) {
     constexpr int kTile = 512;
     const int lane = threadIdx.x & 63;
@@ -818,7 +818,6 @@ __device__ __forceinline__ void sweep_wave(const ReduceArgs& a, int64_t t0) {
     // overlap the two (the grouped 128-way reduction of the GPT-175B shard, rocprofv3:
     // 535-541 us against 557-577 us for explicit overlapped, copy-and-wait and
     // unconditional-reload versions).
-    constexpr int kA = kHybrid ? kGroupSweepAhead : kSweepAhead;
     u4 x[kA][kV];
 #pragma unroll
     for (int q = 0; q < kA; ++q) {
@@ -887,7 +886,7 @@ __device__ __forceinline__ void sweep_wave(const ReduceArgs& a, int64_t t0) {
     }
 }
 
-template <int kPre, bool kAccum, bool kHybrid, int kV>
+template <int kPre, bool kAccum, bool kHybrid, int kV, int kA>
 __global__ __launch_bounds__(64) void reduce_sweep_kernel(SweepArgs s) {
     const ReduceArgs& a = s.r;
     constexpr int64_t kTile = 512;
@@ -913,7 +912,7 @@ __global__ __launch_bounds__(64) void reduce_sweep_kernel(SweepArgs s) {
             a, (s.t_first + b) * kTile + 8 * static_cast<int64_t>(threadIdx.x));
         return;
     }
-    sweep_wave<kPre, kAccum, kHybrid, kV>(a, s.t_first + s.n_single + (b - s.n_single) * kV);
+    sweep_wave<kPre, kAccum, kHybrid, kV, kA>(a, s.t_first + s.n_single + (b - s.n_single) * kV);
 }
 
 // ---------------------------------------------------------------------------
@@ -1292,9 +1291,8 @@ hipError_t launch_segcopy(const std::vector<CopySeg>& segs, Pipe pipe, hipStream
 // Workgroups of a reduce_sweep_kernel instantiation resident at once on the current device
 // (occupancy per CU times CUs), queried once per device; 0 if unknown.
 constexpr int kMaxDevices = 64;
-template <int kPre, bool kAccum, bool kHybrid>
+template <int kPre, bool kAccum, bool kHybrid, int kV, int kA>
 int64_t sweep_capacity() {
-    constexpr int kV = kHybrid ? kGroupSweepV : kSweepV;
     static std::atomic<int64_t> cap[kMaxDevices];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
@@ -1302,7 +1300,7 @@ int64_t sweep_capacity() {
     if (c == 0) {
         int per_cu = 0, cus = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(&reduce_sweep_kernel<kPre, kAccum, kHybrid, kV>),
+                &per_cu, reinterpret_cast<const void*>(&reduce_sweep_kernel<kPre, kAccum, kHybrid, kV, kA>),
                 64, 0) != hipSuccess ||
             hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -1316,13 +1314,12 @@ int64_t sweep_capacity() {
 // grids are resident at once), in output order; *err gets the first launch error.  Returns
 // false, having launched nothing, when the output holds fewer whole tiles than a sweep wave
 // or the occupancy is unknown.
-template <int kPre, bool kAccum, bool kHybrid>
+template <int kPre, bool kAccum, bool kHybrid, int kV, int kA>
 bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
-    constexpr int kV = kHybrid ? kGroupSweepV : kSweepV;
     constexpr int64_t kTile = 512;
     std::vector<SweepRun> runs;
     if (!plan_sweep_runs(a.len / kTile, a.len % kTile != 0, kV,
-                         sweep_capacity<kPre, kAccum, kHybrid>(), &runs))
+                         sweep_capacity<kPre, kAccum, kHybrid, kV, kA>(), &runs))
         return false;
     for (const SweepRun& r : runs) {
         SweepArgs s{};
@@ -1330,7 +1327,7 @@ bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
         s.t_first = r.t_first;
         s.cut = r.cut;
         s.n_single = r.n_single;
-        hipLaunchKernelGGL((reduce_sweep_kernel<kPre, kAccum, kHybrid, kV>),
+        hipLaunchKernelGGL((reduce_sweep_kernel<kPre, kAccum, kHybrid, kV, kA>),
                            dim3(static_cast<unsigned>(r.blocks)), dim3(64), 0, stream, s);
         *err = hipGetLastError();
         if (*err != hipSuccess) break;
@@ -1338,32 +1335,44 @@ bool try_sweep(const ReduceArgs& a, hipStream_t stream, hipError_t* err) {
     return true;
 }
 
-// The flat sum takes the grouped shape where its runs are long, and runs there as one group
-// that spans every rank: the group's sum is the running sum, carried in and out where the
-// flat path carries its total, and the last launch ends the group, whose sum then becomes the
-// total as it is (no total came before it).  Per output the operations and their order are
-// the flat ones.  rocprofv3, cold cache, the grouped against the wide shape in TB/s: 128 ranks
-// over 14.2 M outputs (two runs of 13,825 tiles) 6.66 against 6.46, over 26.2 M (four runs)
-// 6.54 against 6.28; 64 ranks 6.53 / 6.35 and 6.35 / 6.19; 32 ranks 6.15 / 6.17 and 5.99 /
-// 5.97; but over 8.4 M outputs, two runs of 8,192 tiles, 5.36 against 6.55 at 128 ranks.
-template <int kPre>
-bool launch_reduce_sweep(const ReduceArgs& a, bool hybrid, bool accum, hipStream_t stream,
-                         hipError_t* err) {
-    if (hybrid)
-        return accum ? try_sweep<kPre, true, true>(a, stream, err) : try_sweep<kPre, false, true>(a, stream, err);
+// Which shape: the grouped one with two ranks in flight where its runs are long (the flat
+// sum as one group that spans every rank: the group's sum is the running sum, carried in and
+// out where the flat path carries its total, and the last launch ends the group, whose sum
+// then becomes the total as it is, no total having come before it; per output the operations
+// and their order are the flat ones).  Otherwise the wide shape for a flat sum and the grouped
+// one with one rank in flight for a hybrid one.  rocprofv3, cold cache, in TB/s, flat sums:
+// the grouped against the wide shape, 128 ranks over 14.2 M outputs (two runs of 13,825
+// tiles) 6.66 against 6.46, over 26.2 M (four runs) 6.54 against 6.28; 64 ranks 6.53 / 6.35
+// and 6.35 / 6.19; 32 ranks 6.15 / 6.17 and 5.99 / 5.97; but over 8.4 M outputs, two runs of
+// 8,192 tiles, 5.36 against 6.55 at 128 ranks.  Hybrid groups of 8, accumulating, two ranks in
+// flight against one, 128 ranks: 3.5 M outputs (one run of 6,912 tiles) 4.85 against 6.52,
+// 7.1 M (13,824) 6.63-6.67 against 6.47, 8.4 M (two runs of 8,192) 5.37 against 6.31, 14.2 M
+// 6.63-6.65 against 6.50; 256 ranks alike.
+template <int kPre, bool kAccum>
+bool launch_reduce_sweep_t(const ReduceArgs& a, bool hybrid, hipStream_t stream, hipError_t* err) {
+    constexpr int kLong = kGroupSweepLongAhead;
     std::vector<SweepRun> runs;
-    const int64_t cap = accum ? sweep_capacity<kPre, true, true>() : sweep_capacity<kPre, false, true>();
-    if (plan_sweep_runs(a.len / 512, a.len % 512 != 0, kGroupSweepV, cap, &runs) &&
+    if (plan_sweep_runs(a.len / 512, a.len % 512 != 0, kGroupSweepV,
+                        sweep_capacity<kPre, kAccum, true, kGroupSweepV, kLong>(), &runs) &&
         runs.back().n_tiles >= kGroupSweepMinRunTiles) {  // the last run is the shortest
+        if (hybrid) return try_sweep<kPre, kAccum, true, kGroupSweepV, kLong>(a, stream, err);
         ReduceArgs g = a;
         g.flags = (a.flags & kLast) | ((a.flags & kTIn) ? kSIn : 0u) | ((a.flags & kTOut) ? kSOut : 0u);
         g.carry_s = a.carry_t;
         g.carry_t = nullptr;
         g.pos0 = (a.flags & kTIn) ? 1 : 0;  // a carried-in sum is continued, not restarted
         g.group = g.pos0 + a.nc + ((a.flags & kLast) ? 0 : 1);
-        return accum ? try_sweep<kPre, true, true>(g, stream, err) : try_sweep<kPre, false, true>(g, stream, err);
+        return try_sweep<kPre, kAccum, true, kGroupSweepV, kLong>(g, stream, err);
     }
-    return accum ? try_sweep<kPre, true, false>(a, stream, err) : try_sweep<kPre, false, false>(a, stream, err);
+    if (hybrid) return try_sweep<kPre, kAccum, true, kGroupSweepV, 1>(a, stream, err);
+    return try_sweep<kPre, kAccum, false, kSweepV, 1>(a, stream, err);
+}
+
+template <int kPre>
+bool launch_reduce_sweep(const ReduceArgs& a, bool hybrid, bool accum, hipStream_t stream,
+                         hipError_t* err) {
+    return accum ? launch_reduce_sweep_t<kPre, true>(a, hybrid, stream, err)
+                 : launch_reduce_sweep_t<kPre, false>(a, hybrid, stream, err);
 }
 
 template <int kPre>

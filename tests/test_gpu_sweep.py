@@ -106,6 +106,30 @@ def test_sweep_runs_over_several_launches(group, tiles, tail):
     assert_f32_tol_then_bits(to_host(out), want, "sweep runs group=%d S=%d" % (group, S))
 
 
+@pytest.mark.parametrize("N,group,tiles,accumulate", [
+    (288, 144, 14336, True),   # groups longer than a launch: partial group sums carried
+    (256, 8, 13000, False),    # groups of 8 in two launches of 16 groups each
+    (128, 8, 16384, True),     # runs of 8,192 tiles: one rank in flight
+])
+def test_hybrid_sweep_shapes_and_carries(N, group, tiles, accumulate):
+    """Hybrid sums on the grouped sweep: runs of at least 12,288 tiles take the shape with two
+    ranks in flight, shorter ones the shape with one; across launches the total and the partial
+    group sums travel through the caller's workspace exactly."""
+    S = tiles * TILE + 45
+    u = B.fsdp_unit_create(B.FSDP_FLAT, [(N * S,)], N)
+    c, ch = _contribs(N, S, step=12)
+    old = W.host_normal(S, 1e-3, seed=24)
+    out = to_dev(old) if accumulate else torch.full((S,), float("nan"), device=dev())
+    need = B.fsdp_grad_reduce_workspace(u, group=group, accumulate=accumulate)
+    ws = torch.full((need,), float("nan"), device=dev()) if need else None
+    B.fsdp_grad_reduce_shard_ex(u, [c[r] for r in range(N)], 4.0, 16.0, out, group=group,
+                                accumulate=accumulate, kernel="sweep", workspace=ws)
+    torch.cuda.synchronize()
+    want = oracle.grad_reduce_ex(list(ch), 4.0, 16.0, group=group,
+                                 out=old if accumulate else None)
+    assert_f32_tol_then_bits(to_host(out), want, "hybrid sweep N=%d group=%d" % (N, group))
+
+
 @pytest.mark.parametrize("N,tiles", [(160, MIN_TILES), (130, MIN_TILES), (300, MIN_TILES),
                                      (160, 20000)])
 def test_sweep_chained_over_more_than_128_ranks(N, tiles):
