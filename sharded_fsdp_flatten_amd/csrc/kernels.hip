@@ -21,8 +21,9 @@
 //     (src, dst, length[, block stride]) segments passed in the kernel argument
 //     block; each workgroup takes one tile of one segment (the tile -> segment
 //     lookup is wave-uniform, on scalar registers: the segment with the most tiles
-//     is loaded with the table's header, the others found by a binary search), so
-//     no lane ever searches and every tile is a straight streaming copy.  Launches of
+//     and every segment's first tile are loaded with the table's header, and the
+//     others are found by counting), so no lane ever searches and every tile is a
+//     straight streaming copy.  Launches of
 //     2^18 tiles or more hand each XCD runs of 256 consecutive tiles.  When source
 //     and destination are not 16-byte co-aligned, a scalar head aligns the
 //     destination and the source is read in place with dword-aligned 16-byte
@@ -271,15 +272,16 @@ struct DevSeg {
     int64_t src_stride, dst_stride;
 };
 // A launch's segments, passed by value in the kernel-argument block: a table of kCap entries,
-// the smallest of 1, 4, 16 and kMaxSegs that holds the launch's segments, and a copy of the
-// segment with the most tiles next to the header.
+// the smallest of 1, 4, 16 and kMaxSegs that holds the launch's segments, with the segments'
+// first tiles in one array next to the header and a copy of the segment with the most tiles.
 template <int kCap>
 struct SegTable {
     uint32_t ntiles;
     uint32_t nseg;
-    uint32_t xcd_runs;   // tiles in XCD-chunked order (xcd_chunked)
-    uint32_t hot_tiles;  // tiles of `hot`
-    DevSeg hot;          // the segment with the most tiles (unused in one-segment tables)
+    uint32_t xcd_runs;      // tiles in XCD-chunked order (xcd_chunked)
+    uint32_t hot_tiles;     // tiles of `hot`
+    uint32_t start[kCap];   // seg[i].tile0; 0xFFFFFFFF past nseg
+    DevSeg hot;             // the segment with the most tiles (unused in one-segment tables)
     DevSeg seg[kCap];
 };
 static_assert(sizeof(SegTable<kMaxSegs>) <= 4096, "segment table must fit one kernel argument block");
@@ -412,33 +414,40 @@ __device__ __forceinline__ void copy_tile(const DevSeg& sg, uint32_t local, SrcT
 // the kernel reads everything most tiles need in one round trip: the empty asm statements pin
 // the loads at the start, where the compiler would issue each just before its first use,
 // after the previous one's wait.  A one-segment table loads that segment with the header; a
-// larger one loads the copy of its segment with the most tiles, and only the tiles outside it
-// search the table.  GPT-175B block, rank flatten, rocprofv3 durations (cold cache, two rounds
-// on one box): one segment 18.72-18.84 us against 19.04-19.28 with the search for every tile;
-// rank 0's five segments (four LayerNorm tensors of 12 tiles before the big one) 19.20 against
-// 20.16-20.40.
+// larger one loads the copy of its segment with the most tiles and the segments' first tiles,
+// and only the tiles outside the big segment look up theirs: a count on scalar registers,
+// then one load.  GPT-175B block, rank flatten, rocprofv3 durations (cold cache, two rounds
+// on one box): one segment 18.72-18.84 us against 19.04-19.28 with a binary search of the
+// table for every tile; rank 0's five segments (four LayerNorm tensors of 12 tiles before the
+// big one) 19.20 against 20.16-20.40.  Counting instead of the binary search (a dependent load
+// per step) for the tiles outside the big segment, rocprofv3, two rounds of alternating
+// processes each: GPT-2-L block copy-out 20.34-20.52 against 21.08-21.30 us, FSDP2 rows unit
+// flatten 14.88-15.06 against 15.16-15.48 us, larger copies unchanged.
 template <typename SrcT, typename DstT, bool kGeneral, int kCap>
 __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable<kCap> t) {
     constexpr int kTile = tile_elems<SrcT, DstT>();
     __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral && sizeof(SrcT) == 2 ? kTile + 16 : 8];
-    const uint32_t ntiles = t.ntiles, nseg = t.nseg, xcdr = t.xcd_runs;
+    const uint32_t ntiles = t.ntiles, xcdr = t.xcd_runs;
     const DevSeg& z = kCap == 1 ? t.seg[0] : t.hot;
     const uint32_t hot_tiles = kCap == 1 ? ntiles : t.hot_tiles;
-    asm volatile("" ::"s"(ntiles), "s"(nseg), "s"(xcdr), "s"(hot_tiles), "s"(z.src), "s"(z.dst),
+    asm volatile("" ::"s"(ntiles), "s"(xcdr), "s"(hot_tiles), "s"(z.src), "s"(z.dst),
                  "s"(z.blk_n), "s"(z.last_n), "s"(z.nblk), "s"(z.tiles_per_blk), "s"(z.tile0),
                  "s"(z.src_stride), "s"(z.dst_stride));
+    if constexpr (kCap > 1 && kCap <= 16) {
+#pragma unroll
+        for (int i = 1; i < kCap; ++i) asm volatile("" ::"s"(t.start[i]));
+    }
     const uint32_t tile = xcdr ? xcd_chunked<kXcdChunk>(blockIdx.x, ntiles) : blockIdx.x;
     if (kCap == 1 || tile - z.tile0 < hot_tiles) {
         copy_tile<SrcT, DstT, kGeneral>(z, tile - z.tile0, lds);
         return;
     }
-    // wave-uniform binary search of the segment holding this tile
-    uint32_t lo = 0, hi = nseg - 1;
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) >> 1;
-        if (t.seg[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
-    }
-    const DevSeg& sg = t.seg[lo];
+    // the segment holding this tile (wave-uniform): the number of later segments that start
+    // at or before it, counted on scalar registers from starts loaded with the header
+    uint32_t k = 0;
+#pragma unroll
+    for (int i = 1; i < kCap; ++i) k += t.start[i] <= tile ? 1u : 0u;
+    const DevSeg& sg = t.seg[k];
     copy_tile<SrcT, DstT, kGeneral>(sg, tile - sg.tile0, lds);
 }
 
@@ -1073,8 +1082,10 @@ void launch_table(const SegTable<kMaxSegs>& full, bool general, uint64_t tiles, 
     t.nseg = full.nseg;
     t.xcd_runs = full.xcd_runs;
     uint32_t hot = 0;
+    for (int i = 0; i < kCap; ++i) t.start[i] = 0xFFFFFFFFu;
     for (uint32_t i = 0; i < full.nseg; ++i) {
         t.seg[i] = full.seg[i];
+        t.start[i] = full.seg[i].tile0;
         const uint32_t end = i + 1 < full.nseg ? full.seg[i + 1].tile0 : full.ntiles;
         if (end - full.seg[i].tile0 > t.hot_tiles) {
             t.hot_tiles = end - full.seg[i].tile0;
