@@ -12,17 +12,18 @@ and every byte counted comes from HBM.  Inputs are synthetic (seeded normals in
 the unit's shapes) and already resident in HBM when the timed region starts.
 
 Default workload: GPT-175B style block unit (d = 12288, 1,812,099,072 fp32
-elements), FSDP1 flat sharding over N = 128, rank 63; the 128 contributions sit
-in one receive buffer with rows at the library's recommended pitch (S rounded
-up to whole 128-byte lines).
+elements), FSDP1 flat sharding over N = 128, at the rank whose flatten a rank
+sweep (ranks 0, 1, 63, 127) measured slowest; the 128 contributions sit in one
+receive buffer with rows at the library's recommended pitch (S rounded up to
+whole 128-byte lines).
 
 Prints one JSON line (metric, value in GB/s over the whole step, per-kernel
 GB/s, fraction of the 8 TB/s HBM peak and elements/s, the roofline of the
 dominant kernel, and the CPU oracle timed on a bounded sample as a baseline).
-The step is timed from replays of a HIP graph that records its four launches
-once (when no cache flush is needed between kernels, as for the default unit);
-the eager loop, one host call and an event pair per kernel, gives the
-per-kernel times and is reported beside it.
+The step is timed from replays of a HIP graph that records its launches once
+(when no cache flush is needed between kernels, as for the default unit); the
+eager loop, one host call and an event pair per call, gives the per-kernel
+times and is reported beside it.
 """
 from __future__ import annotations
 
@@ -79,7 +80,7 @@ def parse_args():
     ap.add_argument("--no-sweep-ranks", dest="sweep_ranks", action="store_false",
                     help="skip the rank sweep")
     ap.add_argument("--graph", default="auto", choices=["auto", "on", "off"],
-                    help="replay the step from a captured HIP graph (the four launches recorded once, "
+                    help="replay the step from a captured HIP graph (its launches recorded once, "
                          "no host launch overhead per step).  auto: on when no flush is needed, and "
                          "then `value` comes from the graph replays (the eager loop with per-kernel "
                          "events is reported beside it); with a flush the graph is only reported")
@@ -735,9 +736,10 @@ def main():
                    "step_time": ("sum of the kernels' event times, 1 GiB read before each kernel"
                                  if flush_on else "wall clock")},
         "kernels": kernels,
-        "kernel_timing": ("HIP events recorded around each launch on its stream in the eager loop; "
-                          "an event pair adds 2-5 us, a few percent on the short kernels (flatten, "
-                          "AdamW); rocprofv3 kernel durations are in profiles/"),
+        "kernel_timing": ("HIP events recorded around each call on its stream in the eager loop "
+                          "(a reduction on the grouped sweep is one call of two launches); an event "
+                          "pair adds 2-5 us, a few percent on the short kernels (flatten, AdamW); "
+                          "rocprofv3 kernel durations are in profiles/"),
         "kernel_src_sha256": kernel_src_hash(),
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
