@@ -100,6 +100,11 @@ def parse_args():
                     help="also time the reduction on the tile kernel and on the row-major sweep "
                          "alone and while a stream of bf16 GEMMs (a backward pass's compute) runs "
                          "on a second stream of the same priority")
+    ap.add_argument("--reduce-shapes", action="store_true",
+                    help="also time the reduction on the tile kernel and on the row-major sweep "
+                         "over 32, 64 and 128 ranks at 4.2 M to 26.2 M outputs (flat sums) and over "
+                         "128 ranks in groups of 8, accumulating, at 3.5 M to 14.2 M outputs: 8 "
+                         "launches each after a 1 GiB read, for rocprofv3's kernel trace")
     return ap.parse_args()
 
 
@@ -511,6 +516,55 @@ def flatten_floor(B, u, N, params, stream, dev, gen, reps=20):
     return out
 
 
+REDUCE_SHAPES_FLAT = [(n, s) for n in (32, 64, 128) for s in (4 << 20, 8 << 20, 14157024, 25 << 20)]
+REDUCE_SHAPES_HYBRID = [(128, s) for s in (3538944, 7077888, 8 << 20, 14157024)]
+
+
+def reduce_shapes(B, stream, dev, gen, reps=8):
+    """The reduction on the tile kernel and on the sweep (whose shape the library picks by the
+    length of its runs) over several rank counts and output lengths: flat sums, and hybrid
+    accumulating sums in groups of 8.  Contributions are seeded normals (std 1e-3) in one
+    receive buffer at the recommended pitch; every launch follows a 1 GiB read.  Event medians
+    (ms) are reported; rocprofv3's kernel trace of the same run gives the kernel durations."""
+    import torch
+    fb = torch.zeros(1 << 28, device=dev)
+    fs = torch.zeros((), device=dev)
+
+    def flush():
+        torch.sum(fb, dim=0, out=fs)
+
+    out = []
+    for group, shapes in ((0, REDUCE_SHAPES_FLAT), (8, REDUCE_SHAPES_HYBRID)):
+        for n, s in shapes:
+            u = B.fsdp_unit_create(B.FSDP_FLAT, [(n * s,)], n)
+            buf = torch.empty((n, u.recv_pitch), dtype=torch.bfloat16, device=dev)
+            c = buf[:, :s]
+            c.normal_(0.0, 1e-3, generator=gen)
+            rows = [c[r] for r in range(n)]
+            grad = torch.zeros(s, device=dev)
+            accumulate = group > 0
+            need = B.fsdp_grad_reduce_workspace(u, group=group, accumulate=accumulate)
+            ws = torch.zeros(need, device=dev) if need else None
+            row = {"ranks": n, "outputs": s, "group": group, "accumulate": accumulate,
+                   "bytes": (2 * n + (8 if accumulate else 4)) * s}
+            for kernel in ("tiles", "sweep"):
+                def call():
+                    B.fsdp_grad_reduce_shard_ex(u, rows, 2.0, 4.0, grad, group=group,
+                                                accumulate=accumulate, kernel=kernel, workspace=ws)
+                flush()
+                call()  # untimed: the sweep's first call per shape reads the device's occupancy
+                ms = _event_median(call, stream, reps, before=flush)
+                row[kernel] = {"event_ms_median": round(ms, 4),
+                               "GB/s": round(row["bytes"] / (ms * 1e-3) / 1e9, 1)}
+            out.append(row)
+            print("reduce shapes: N=%d S=%d group=%d done" % (n, s, group), file=sys.stderr,
+                  flush=True)
+            del buf, c, rows, grad, ws
+            torch.cuda.empty_cache()
+    del fb
+    return out
+
+
 def contention_probe(B, u, N, contrib_rows, pre, post, grad, stream, dev, reps=10):
     """The reduction on the tile kernel and on the row-major sweep, alone and overlapped with a
     stream of bf16 GEMMs on a second stream of the same priority (the backward compute that the
@@ -821,6 +875,8 @@ def main():
         result["flatten_floor"] = flatten_floor(B, u, N, params, stream, dev, gen)
     if args.contention_probe:
         result["contention"] = contention_probe(B, u, N, contrib_rows, pre, post, grad, stream, dev)
+    if args.reduce_shapes:
+        result["reduce_shapes"] = reduce_shapes(B, stream, dev, gen)
     if args.floor_probe:
         fb = torch.zeros(1 << 28, device=dev)
         fs = torch.zeros((), device=dev)

@@ -107,3 +107,21 @@ def test_bench_defaults_probes_and_opt_outs():
     assert p.returncode == 0, p.stderr[-2000:]
     d = json.loads([l for l in p.stdout.splitlines() if l.startswith("{")][0])
     assert "per_rank" not in d
+
+
+def test_bench_reduce_shapes_probe():
+    """The reduction-shape probe reports both kernels for every flat and hybrid shape it runs,
+    with the bytes of each reduction."""
+    p = _run("--workload", "tiny", "--steps", "1", "--warmup", "1", "--no-cpu-baseline",
+             "--no-next", "--no-sweep-ranks", "--reduce-shapes", timeout=300)
+    assert p.returncode == 0, p.stderr[-2000:]
+    d = json.loads([l for l in p.stdout.splitlines() if l.startswith("{")][0])
+    import bench
+    rs = d["reduce_shapes"]
+    assert [(r["ranks"], r["outputs"]) for r in rs if r["group"] == 0] == bench.REDUCE_SHAPES_FLAT
+    assert [(r["ranks"], r["outputs"]) for r in rs if r["group"] == 8] == bench.REDUCE_SHAPES_HYBRID
+    for r in rs:
+        assert r["bytes"] == (2 * r["ranks"] + (8 if r["accumulate"] else 4)) * r["outputs"]
+        assert r["accumulate"] == (r["group"] > 0)
+        for k in ("tiles", "sweep"):
+            assert r[k]["event_ms_median"] > 0 and r[k]["GB/s"] > 0
