@@ -24,7 +24,7 @@
 //     and every segment's first tile are loaded with the table's header, and the
 //     others are found by counting), so no lane ever searches and every tile is a
 //     straight streaming copy.  Launches of
-//     2^18 tiles or more hand each XCD runs of 256 consecutive tiles.  When source
+//     2^15 tiles or more hand each XCD runs of 256 consecutive tiles.  When source
 //     and destination are not 16-byte co-aligned, a scalar head aligns the
 //     destination and the source is read in place with dword-aligned 16-byte
 //     loads; only a bf16 source at an odd element offset is staged through LDS.
@@ -88,9 +88,12 @@ constexpr int kTileStoreCpol = 18;
 // kXcdChunk consecutive tiles instead of every eighth tile.  Copy-out (885k tiles):
 // dispatch order 6.46-6.49, one contiguous run per XCD 6.61-6.65, runs of 64 / 128 / 256 /
 // 512 tiles 6.65-6.67 / 6.76 / 6.76-6.78 / 6.62-6.63.  One run per XCD made 64-256 MB
-// copies 3-7% slower; runs of 256 left every size from 8 MB to 1 GB as fast as the
-// dispatch order.
-constexpr uint32_t kXcdMinTiles = 1u << 18;
+// copies 3-7% slower.  From 2^15 tiles on (rocprofv3, alternating processes, against 2^18):
+// the T5 block's copy-out (98k tiles) 177.8-181.6 against 186.3-189.4 us, its local
+// accumulation 306-325 against 328-332 us, the FSDP2 rows copy-out (41k tiles) 75.6-78.2
+// against 79.4-80.1 us, fp32 copies of 268 MB - 1 GB 1-2% faster; 2^14 (which also takes
+// the T5 rank flatten, 25k tiles) measured the same as 2^15.
+constexpr uint32_t kXcdMinTiles = 1u << 15;
 constexpr uint32_t kXcdChunk = 256u;
 constexpr int kReduceThreads = 64;   // reduction tile kernel: one wave per 512-output tile
 constexpr int kReduceAhead = 8;      // ranks loaded before their adds in the tile kernel
@@ -935,7 +938,7 @@ __global__ __launch_bounds__(64) void reduce_sweep_kernel(SweepArgs s) {
 // (exchanged across lanes with ds_bpermute, no LDS allocation).  Against 8-byte bf16 loads
 // with 4 elements per lane (4 per lane and vector, 4 vectors: 6.02-6.07 TB/s over the
 // GPT-175B unit's 1.8 G elements) this measured 6.32-6.34 TB/s; with 16-byte fp32 accesses
-// at a 32-byte stride instead of the exchange 5.32-5.52.  Grids of 2^18 blocks or more hand
+// at a 32-byte stride instead of the exchange 5.32-5.52.  Grids of 2^15 blocks or more hand
 // each XCD runs of kAccXcdChunk blocks.
 template <bool kInit, bool kVec>
 __global__ __launch_bounds__(kThreads) void accumulate_kernel(const uint16_t* __restrict__ g,
