@@ -34,11 +34,12 @@
 //     whole tiles swap halves across lanes so each store writes 1 KiB; the tile
 //     the output's end cuts runs first, its last len % 8 outputs one per lane.
 //     From 32 ranks and 12,288 whole tiles on, a row-major sweep instead: each
-//     wave holds 16 tiles' sums with one rank in flight, or 8 tiles' group sums
-//     and totals with two ranks in flight (hybrid groups; the flat sum as one
-//     group where that shape's runs are long), and walks the ranks in order, the
-//     grid sized to be resident at once (each XCD one contiguous run of waves),
-//     so HBM serves a few contribution rows at a time.  More ranks than one launch holds (128) take several launches that
+//     wave holds 16 tiles' sums with one rank in flight (flat sums), or 8 tiles'
+//     group sums and totals with two ranks in flight where the runs are long
+//     (hybrid sums, and flat ones as a single group) and one where they are
+//     short, and walks the ranks in order, the grid sized to be resident at once
+//     (each XCD one contiguous run of waves), so HBM serves a few contribution
+//     rows at a time.  More ranks than one launch holds (128) take several launches that
 //     carry their exact running sums through the output or a caller's workspace.
 //   - adamw: elementwise over 8 elements per lane, 128-bit loads and stores.
 //     Its state is read and written back in place: plain loads measure faster
@@ -105,7 +106,7 @@ constexpr int kReduceAhead = 8;      // ranks loaded before their adds in the ti
 // 90.1 us), the GPT-175B hybrid accumulating reduction on this kernel 570.7-572.1 against
 // 594.5-595.9 us; the GPT-2-L block's 10.5-10.6 us either way.
 constexpr unsigned kReduceLdsCap = 5632;
-constexpr int kSweepMinRanks = 32;   // the flat reduction sweeps ranks row-major from this many
+constexpr int kSweepMinRanks = 32;   // by default a launch sweeps ranks row-major from this many
 constexpr int kSweepMinTiles = 12288;  // ... and from this many whole 512-output tiles on
 // Shapes of the sweep.  The wide one (flat sums) holds 16 tiles' sums per wave and one rank
 // in flight (8/12/16 tiles: 6.23/6.36/6.53 TB/s).  The grouped ones hold 8 tiles' group sums
