@@ -351,7 +351,8 @@ FSDP_API fsdp_status fsdp_flatten_shard_bf16(const fsdp_unit* unit, const uint16
  * when it must keep its old value (accumulate) or a group is longer than one
  * launch: then they go to the caller's workspace (see
  * fsdp_grad_reduce_workspace; calls that share a workspace on one stream run
- * in order, on different streams they must not share one).
+ * in order, on different streams they must not share one).  The workspace
+ * must not overlap grad_shard or any contribution (not checked).
  * Errors as fsdp_grad_reduce_shard, plus FSDP_E_ARG (opts NULL; workspace NULL
  * when one is needed), FSDP_E_RANGE (group does not divide N; kernel not an
  * fsdp_reduce_kernel; workspace_len below what is needed) and FSDP_E_ALIGN
