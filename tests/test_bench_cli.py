@@ -93,3 +93,55 @@ def test_committed_counter_traffic_matches_the_algorithmic_bytes():
     assert len(scales) == 3
     for f, w in scales:
         assert abs(f / scales[0][0] - 1) < 1e-4 and abs(w / scales[0][1] - 1) < 1e-4
+
+
+def test_all_cores_baseline_slices_reassemble_the_single_call_results():
+    """The all-cores CPU baseline runs the unchanged oracle on disjoint output slices from
+    several threads; its claim that the results are those of one call rests on the slicing.
+    Here the slices of each part (flatten of a rank, copy-out of the unit, reduction, AdamW),
+    cut exactly as the baseline cuts them, are reassembled and compared bit for bit with one
+    call over the whole range, for a padded unit and a rank whose shard straddles parameters."""
+    import numpy as np
+
+    import bench
+    import oracle
+    import workloads as W
+
+    unit = W.gpt2_large_block(N=8)
+    N, k, threads = 7, 3, 5  # N = 7 pads the flat buffer; 5 threads cut uneven slices
+    params = W.host_params(unit, seed=1)
+    numels = [int(np.prod(s)) if len(s) else 1 for s in unit.shapes]
+    T = sum(numels)
+    S = -(-T // N)
+    whole = oracle.flat_shard(params, N, k)
+    real = min(S, max(0, T - k * S))
+    pieces = [oracle.flat_shard(bench._flat_pieces(params, numels, k * S + a, k * S + b), 1, 0)
+              for a, b in bench._slices(real, threads)]
+    assert np.array_equal(np.concatenate(pieces).view(np.uint32), whole[:real].view(np.uint32))
+
+    gathered = oracle.flat_shard(params, N, -1)
+    want = np.concatenate([o.reshape(-1) for o in oracle.flat_copyout(unit.shapes, gathered)])
+    got = np.concatenate([o.reshape(-1)
+                          for a, b in bench._slices(T, threads)
+                          for o in oracle.flat_copyout(
+                              [(x.size,) for x in bench._flat_pieces(params, numels, a, b)],
+                              gathered[a:b])])
+    assert np.array_equal(got, want)
+
+    n_red = 12345
+    c = W.host_contribs(N, n_red, step=2)
+    want = oracle.grad_reduce([c[r] for r in range(N)], 2.0, 3.0)
+    got = np.concatenate([oracle.grad_reduce([c[r, a:b] for r in range(N)], 2.0, 3.0)
+                          for a, b in bench._slices(n_red, threads)])
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+    hp = dict(lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.01)
+    p0 = W.host_normal(9999, 0.02, seed=3)
+    g = W.host_normal(9999, 1e-3, seed=4)
+    p1, m1, v1 = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+    oracle.adamw(p1, g, m1, v1, step=1, **hp)
+    p2, m2, v2 = p0.copy(), np.zeros_like(p0), np.zeros_like(p0)
+    for a, b in bench._slices(p0.size, threads):
+        oracle.adamw(p2[a:b], g[a:b], m2[a:b], v2[a:b], step=1, **hp)
+    for x, y in ((p1, p2), (m1, m2), (v1, v2)):
+        assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
