@@ -1224,15 +1224,21 @@ struct SqRun {
     int32_t out;      // parameter index
     int32_t unused;
 };
+// A launch's runs, passed by value in the kernel-argument block: a table of kCap entries (1, 4,
+// 16 or kMaxSegs), with the runs' first tiles in one array next to the header and a copy of the
+// run with the most tiles, for the lookup of the copy engine's segment table.
+template <int kCap>
 struct SqTable {
     const float* g;
     double* partial;
     double* out;
     uint32_t nrun;
     uint32_t unused;
-    SqRun run[kMaxSegs];
+    uint32_t start[kCap];  // run[i].tile0; 0xFFFFFFFF past nrun
+    SqRun hot;             // the run with the most tiles (unused in one-run tables)
+    SqRun run[kCap];
 };
-static_assert(sizeof(SqTable) <= 4096, "run table must fit one kernel argument block");
+static_assert(sizeof(SqTable<kMaxSegs>) <= 4096, "run table must fit one kernel argument block");
 
 // Block sum of one double per thread, in a fixed order: a shuffle tree inside each
 // wave, then the waves' sums in wave order.  Returns the sum in thread 0.
@@ -1250,18 +1256,11 @@ __device__ __forceinline__ double block_sum(double v, double* lds) {
 // Stage 1: one tile of one run per workgroup -> one partial sum.  Each lane adds
 // the squares of its 16 elements in order (a binary32 square is exact in binary64).
 // Loads need dword alignment only (runs start at any element).
-__global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(SqTable t) {
-    __shared__ double lds[kSqThreads / 64];
-    const uint32_t tile = blockIdx.x;
-    uint32_t lo = 0, hi = t.nrun - 1;  // wave-uniform: last non-empty run with tile0 <= tile
-    while (lo < hi) {
-        const uint32_t mid = (lo + hi + 1) >> 1;
-        if (t.run[mid].tile0 <= tile) lo = mid; else hi = mid - 1;
-    }
-    const SqRun& r = t.run[lo];
+__device__ __forceinline__ void sq_tile(const float* g0, double* partial, const SqRun& r,
+                                        uint32_t tile, double* lds) {
     const int64_t e0 = static_cast<int64_t>(tile - r.tile0) * kSqTile;
     const int64_t n = min(kSqTile, r.n - e0);
-    const float* g = t.g + r.offset + e0;
+    const float* g = g0 + r.offset + e0;
     double acc = 0.0;
     if (n == kSqTile) {
         f4 x[kSqPerThread / 4];
@@ -1281,12 +1280,36 @@ __global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(SqTable t) {
         }
     }
     const double s = block_sum(acc, lds);
-    if (threadIdx.x == 0) t.partial[tile] = s;
+    if (threadIdx.x == 0) partial[tile] = s;
+}
+
+// The tile's run is found as the copy engine finds a tile's segment: the header and the run
+// with the most tiles are loaded at the start (pinned there by the empty asm statements), and
+// only tiles outside that run count the later runs that start at or before them.
+template <int kCap>
+__global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(SqTable<kCap> t) {
+    __shared__ double lds[kSqThreads / 64];
+    const uint32_t tile = blockIdx.x;
+    const SqRun& z = kCap == 1 ? t.run[0] : t.hot;
+    asm volatile("" ::"s"(t.g), "s"(t.partial), "s"(z.offset), "s"(z.n), "s"(z.tile0),
+                 "s"(z.ntiles));
+    if constexpr (kCap > 1 && kCap <= 16) {
+#pragma unroll
+        for (int i = 1; i < kCap; ++i) asm volatile("" ::"s"(t.start[i]));
+    }
+    if (kCap == 1 || tile - z.tile0 < z.ntiles) {
+        sq_tile(t.g, t.partial, z, tile, lds);
+        return;
+    }
+    uint32_t k = 0;
+#pragma unroll
+    for (int i = 1; i < kCap; ++i) k += t.start[i] <= tile ? 1u : 0u;
+    sq_tile(t.g, t.partial, t.run[k], tile, lds);
 }
 
 // Stage 2: one workgroup per run sums its partials in a fixed order (lane order
 // within strided passes, then the block tree) and writes the parameter's result.
-__global__ __launch_bounds__(kSqThreads) void sqnorm_final_kernel(SqTable t) {
+__global__ __launch_bounds__(kSqThreads) void sqnorm_final_kernel(SqTable<kMaxSegs> t) {
     __shared__ double lds[kSqThreads / 64];
     const SqRun& r = t.run[blockIdx.x];
     double acc = 0.0;
@@ -1564,6 +1587,30 @@ hipError_t sqnorm_scratch(double** out) {
     return hipSuccess;
 }
 
+namespace {
+
+// Stage 1 over the non-empty runs of `busy` (first tile 0), with the smallest table that holds
+// them.
+template <int kCap>
+void launch_sq_partial(const SqTable<kMaxSegs>& busy, uint32_t tiles, hipStream_t stream) {
+    SqTable<kCap> t{};
+    t.g = busy.g;
+    t.partial = busy.partial;
+    t.out = busy.out;
+    t.nrun = busy.nrun;
+    uint32_t hot = 0;
+    for (int i = 0; i < kCap; ++i) t.start[i] = 0xFFFFFFFFu;
+    for (uint32_t i = 0; i < busy.nrun; ++i) {
+        t.run[i] = busy.run[i];
+        t.start[i] = busy.run[i].tile0;
+        if (busy.run[i].ntiles > busy.run[hot].ntiles) hot = i;
+    }
+    t.hot = busy.run[hot];
+    hipLaunchKernelGGL((sqnorm_partial_kernel<kCap>), grid_of(tiles), dim3(kSqThreads), 0, stream, t);
+}
+
+}  // namespace
+
 int64_t sqnorm_tiles(const std::vector<ParamRun>& runs) {
     int64_t n = 0;
     for (const ParamRun& r : runs) n += (r.n + kSqTile - 1) / kSqTile;
@@ -1576,7 +1623,7 @@ hipError_t launch_grad_sqnorm(const float* g, const std::vector<ParamRun>& runs,
     int64_t slot = 0;
     for (size_t i0 = 0; i0 < runs.size(); i0 += kMaxSegs) {
         const size_t i1 = std::min(runs.size(), i0 + static_cast<size_t>(kMaxSegs));
-        SqTable all{}, busy{};  // every run of the batch / only the non-empty ones
+        SqTable<kMaxSegs> all{}, busy{};  // every run of the batch / only the non-empty ones
         all.g = busy.g = g;
         all.partial = busy.partial = partial;
         all.out = busy.out = out;
@@ -1597,7 +1644,10 @@ hipError_t launch_grad_sqnorm(const float* g, const std::vector<ParamRun>& runs,
             const uint32_t first = busy.run[0].tile0;
             for (uint32_t j = 0; j < busy.nrun; ++j) busy.run[j].tile0 -= first;
             busy.partial = partial + first;
-            hipLaunchKernelGGL(sqnorm_partial_kernel, grid_of(tiles), dim3(kSqThreads), 0, stream, busy);
+            if (busy.nrun == 1) launch_sq_partial<1>(busy, tiles, stream);
+            else if (busy.nrun <= 4) launch_sq_partial<4>(busy, tiles, stream);
+            else if (busy.nrun <= 16) launch_sq_partial<16>(busy, tiles, stream);
+            else launch_sq_partial<kMaxSegs>(busy, tiles, stream);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
