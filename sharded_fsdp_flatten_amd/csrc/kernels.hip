@@ -276,7 +276,7 @@ struct DevSeg {
     int64_t src_stride, dst_stride;
 };
 // A launch's segments, passed by value in the kernel-argument block: a table of kCap entries,
-// the smallest of 1, 4, 16 and kMaxSegs that holds the launch's segments, with the segments'
+// the smallest of 1, 4, 8, 16 and kMaxSegs that holds the launch's segments, with the segments'
 // first tiles in one array next to the header and a copy of the segment with the most tiles.
 template <int kCap>
 struct SegTable {
@@ -426,7 +426,11 @@ __device__ __forceinline__ void copy_tile(const DevSeg& sg, uint32_t local, SrcT
 // big one) 19.20 against 20.16-20.40.  Counting instead of the binary search (a dependent load
 // per step) for the tiles outside the big segment, rocprofv3, two rounds of alternating
 // processes each: GPT-2-L block copy-out 20.34-20.52 against 21.08-21.30 us, FSDP2 rows unit
-// flatten 14.88-15.06 against 15.16-15.48 us, larger copies unchanged.
+// flatten 14.88-15.06 against 15.16-15.48 us, larger copies unchanged.  The first tiles are
+// pinned only in tables of up to 8 entries: with 16 the compiler splits the header's loads into
+// two rounds for every tile.  Five to eight segments take the 8-entry table: the GPT-2-L block's
+// rank 2 (two large segments among five) 5.62-5.76 us against 6.06-6.30 in the 16-entry table,
+// the GPT-175B step unchanged (rocprofv3, three rounds of alternating processes).
 template <typename SrcT, typename DstT, bool kGeneral, int kCap>
 __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable<kCap> t) {
     constexpr int kTile = tile_elems<SrcT, DstT>();
@@ -437,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable<kCap> t) {
     asm volatile("" ::"s"(ntiles), "s"(xcdr), "s"(hot_tiles), "s"(z.src), "s"(z.dst),
                  "s"(z.blk_n), "s"(z.last_n), "s"(z.nblk), "s"(z.tiles_per_blk), "s"(z.tile0),
                  "s"(z.src_stride), "s"(z.dst_stride));
-    if constexpr (kCap > 1 && kCap <= 16) {
+    if constexpr (kCap > 1 && kCap <= 8) {
 #pragma unroll
         for (int i = 1; i < kCap; ++i) asm volatile("" ::"s"(t.start[i]));
     }
@@ -447,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable<kCap> t) {
         return;
     }
     // the segment holding this tile (wave-uniform): the number of later segments that start
-    // at or before it, counted on scalar registers from starts loaded with the header
+    // at or before it
     uint32_t k = 0;
 #pragma unroll
     for (int i = 1; i < kCap; ++i) k += t.start[i] <= tile ? 1u : 0u;
@@ -1145,6 +1149,7 @@ hipError_t launch_segcopy_t(const std::vector<CopySeg>& segs, hipStream_t stream
         t.xcd_runs = tiles >= kXcdMinTiles ? 1u : 0u;
         if (t.nseg <= 1) launch_table<SrcT, DstT, 1>(t, general, tiles, stream);
         else if (t.nseg <= 4) launch_table<SrcT, DstT, 4>(t, general, tiles, stream);
+        else if (t.nseg <= 8) launch_table<SrcT, DstT, 8>(t, general, tiles, stream);
         else if (t.nseg <= 16) launch_table<SrcT, DstT, 16>(t, general, tiles, stream);
         else launch_table<SrcT, DstT, kMaxSegs>(t, general, tiles, stream);
         const hipError_t e = hipGetLastError();
@@ -1225,7 +1230,7 @@ struct SqRun {
     int32_t unused;
 };
 // A launch's runs, passed by value in the kernel-argument block: a table of kCap entries (1, 4,
-// 16 or kMaxSegs), with the runs' first tiles in one array next to the header and a copy of the
+// 8, 16 or kMaxSegs), with the runs' first tiles in one array next to the header and a copy of the
 // run with the most tiles, for the lookup of the copy engine's segment table.
 template <int kCap>
 struct SqTable {
@@ -1293,7 +1298,7 @@ __global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(SqTable<kCap
     const SqRun& z = kCap == 1 ? t.run[0] : t.hot;
     asm volatile("" ::"s"(t.g), "s"(t.partial), "s"(z.offset), "s"(z.n), "s"(z.tile0),
                  "s"(z.ntiles));
-    if constexpr (kCap > 1 && kCap <= 16) {
+    if constexpr (kCap > 1 && kCap <= 8) {
 #pragma unroll
         for (int i = 1; i < kCap; ++i) asm volatile("" ::"s"(t.start[i]));
     }
@@ -1646,6 +1651,7 @@ hipError_t launch_grad_sqnorm(const float* g, const std::vector<ParamRun>& runs,
             busy.partial = partial + first;
             if (busy.nrun == 1) launch_sq_partial<1>(busy, tiles, stream);
             else if (busy.nrun <= 4) launch_sq_partial<4>(busy, tiles, stream);
+            else if (busy.nrun <= 8) launch_sq_partial<8>(busy, tiles, stream);
             else if (busy.nrun <= 16) launch_sq_partial<16>(busy, tiles, stream);
             else launch_sq_partial<kMaxSegs>(busy, tiles, stream);
             const hipError_t e = hipGetLastError();
