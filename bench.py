@@ -213,6 +213,7 @@ def cpu_baseline(host, unit, N, k, S, valid, pre, post, hp, rows):
                    "unit, reduction of the first S/8=%d outputs over all %d ranks, AdamW on the "
                    "whole shard; single-threaded C oracle" % (unit.name, N, k, n_red, N)),
         "cpu_model": host_cpu_model(),
+        "host": host_facts(),
         "per_kernel_gbs": {name: round(b / dt / 1e9, 3) for name, (b, dt) in parts.items()},
         "seconds": round(t_tot, 2),
     }
@@ -244,6 +245,25 @@ def host_cpu_model():
     except OSError:
         pass
     return "unknown"
+
+
+def host_facts():
+    """The host the baseline ran on: logical CPUs the machine has, those this process may use,
+    and its memory."""
+    ram_gb = None
+    try:
+        with open("/proc/meminfo") as f:
+            for line in f:
+                if line.startswith("MemTotal:"):
+                    ram_gb = round(int(line.split()[1]) * 1024 / 1e9, 1)
+                    break
+    except (OSError, ValueError, IndexError):
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"nproc": os.cpu_count(), "usable_cpus": usable, "ram_gb": ram_gb}
 
 
 def cpu_baseline_all_cores(host, unit, N, k, S, valid, pre, post, hp, rows, threads):
@@ -315,6 +335,7 @@ def cpu_baseline_all_cores(host, unit, N, k, S, valid, pre, post, hp, rows, thre
         "per_kernel_gbs": {name: round(b / dt / 1e9, 3) for name, (b, dt) in parts.items()},
         "seconds": round(t_tot, 2),
         "cpu_model": host_cpu_model(),
+        "host": host_facts(),
     }
 
 
