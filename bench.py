@@ -412,7 +412,7 @@ def time_next_rows(B, u, unit, args, N, k, S, L, T, pre, post, contrib_rows, gra
     out["timing"] = ("mean of one HIP event pair around each call, each after the flush when one "
                      "runs; a call's launches are all inside its pair (the sums of squares are two, "
                      "a reduction on the grouped sweep one per run), and the pair adds 2-5 us, "
-                     "most of the time of the shard-sized calls; their kernel durations are in "
+                     "a large share of a shard-sized call; kernel durations without it are in "
                      "the rocprofv3 summaries")
     del rs_input, shard16, sq_ws, sq_out, flag
     return out
