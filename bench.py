@@ -84,9 +84,12 @@ def parse_args():
                          "no host launch overhead per step).  auto: on when no flush is needed, and "
                          "then `value` comes from the graph replays (the eager loop with per-kernel "
                          "events is reported beside it); with a flush the graph is only reported")
-    ap.add_argument("--copy-probe", action="store_true",
-                    help="also time a plain 4 GiB fp32 copy through the library (N = 1 unit) "
-                         "and hipMemcpy device-to-device, as copy ceilings")
+    ap.add_argument("--copy-probe", dest="copy_probe", action="store_true", default=True,
+                    help="time a plain 4 GiB fp32 copy through the library (N = 1 unit) and "
+                         "hipMemcpy device-to-device, as copy ceilings, and give every kernel's "
+                         "rate as a fraction of the faster one (default)")
+    ap.add_argument("--no-copy-probe", dest="copy_probe", action="store_false",
+                    help="skip the copy ceilings")
     ap.add_argument("--floor-probe", action="store_true",
                     help="also split the flatten of one rank shard into what any kernel of its "
                          "shape pays: an empty kernel with the flatten's grid and with one wave, "
@@ -894,7 +897,12 @@ def main():
             ms = e0.elapsed_time(e1) / reps
             probe[name] = {"bytes": 8 * n, "ms": round(ms, 4),
                            "GB/s": round(8 * n / (ms * 1e-3) / 1e9, 1)}
+        ceiling = max(v["GB/s"] for v in probe.values())
+        probe["ceiling_GB/s"] = ceiling
+        probe["timing"] = "ten back-to-back copies between one HIP event pair, after three untimed"
         result["copy_ceiling"] = probe
+        for kd in result["kernels"].values():
+            kd["frac_of_copy_ceiling"] = round(kd["GB/s"] / ceiling, 4)
         del a, b
 
     if args.floor_probe:

@@ -77,6 +77,13 @@ def test_bench_headline_from_graph_replays_without_flush():
     step_bytes = sum(k["bytes"] for k in d["kernels"].values())
     assert abs(d["value"] - step_bytes / (d["ms_per_step"] * 1e-3) / 1e9) <= 0.01 * d["value"] + 0.1
     assert d["eager"]["ms_per_step"] > 0 and "graph" not in d
+    # the copy ceiling is on by default
+    assert d["copy_ceiling"]["ceiling_GB/s"] > 0
+    p = _run("--workload", "tiny", "--steps", "2", "--warmup", "1", "--no-cpu-baseline",
+             "--no-next", "--no-sweep-ranks", "--no-copy-probe")
+    assert p.returncode == 0, p.stderr[-2000:]
+    d = json.loads([l for l in p.stdout.splitlines() if l.startswith("{")][0])
+    assert "copy_ceiling" not in d and all("frac_of_copy_ceiling" not in k for k in d["kernels"].values())
 
 
 def test_bench_defaults_probes_and_opt_outs():
@@ -89,7 +96,11 @@ def test_bench_defaults_probes_and_opt_outs():
     assert "per_rank" in d and "timing" in d["per_rank"] and "kernel_timing" in d
     assert "next_rows" not in d
     cp = d["copy_ceiling"]
-    assert set(cp) == {"library_copy", "hipMemcpyDtoD"} and all(v["GB/s"] > 0 for v in cp.values())
+    runs = {k: v for k, v in cp.items() if isinstance(v, dict)}
+    assert set(runs) == {"library_copy", "hipMemcpyDtoD"} and all(v["GB/s"] > 0 for v in runs.values())
+    assert cp["ceiling_GB/s"] == max(v["GB/s"] for v in runs.values())
+    for k in d["kernels"].values():
+        assert abs(k["frac_of_copy_ceiling"] - k["GB/s"] / cp["ceiling_GB/s"]) < 1e-3
     ff = d["flatten_floor"]
     N = d["config"]["N"]
     assert len(ff["order"]) == 5 + len({0, 1, max(0, N // 2 - 1), N - 1})
