@@ -13,8 +13,8 @@
 //     that matters is over ranks, and a longer run per wave keeps it compact;
 //   - outputs stored non-temporally (streamed, never re-read by the kernel); the
 //     copies' whole tiles with device-scope nt buffer stores, which stream out
-//     faster than the default-scope ones (as do the local accumulation's; AdamW
-//     and the unscale keep default-scope nt stores).
+//     faster than the default-scope ones (as do the local accumulation's and the
+//     reductions' whole tiles; AdamW and the unscale keep default-scope nt stores).
 // The kernels:
 //   - segcopy: one engine for flatten (FSDP1 and FSDP2), copy-out, the cast and
 //     the bf16 copies.  The host planner turns the layout into a short table of
@@ -635,9 +635,17 @@ __device__ __forceinline__ void reduce_one(const ReduceArgs& a, int64_t j) {
 // Stores a wave's 512 outputs of one whole tile, lane l holding outputs 8l .. 8l+7
 // in acc: the halves are swapped across lanes (ds_bpermute, no LDS allocation) so
 // that each store instruction writes 1 KiB of whole cache lines.  lane l stores
-// outputs 4l .. 4l+3 of each 256-output half, which lane 32h + l/2 holds.
+// outputs 4l .. 4l+3 of each 256-output half, which lane 32h + l/2 holds.  The
+// stores are the copies' device-scope nt buffer stores (the 2 KiB block is 16-byte
+// aligned: the whole-tile path runs only on 16-byte-aligned outputs and workspace
+// slots).  Against global nt stores, HIP-event medians, alternating processes on one
+// box: the 8-way tile reduction of 25.2 M outputs 79.9-81.1 against 81.1-82.6 us and of
+// 10.5 M 38.2-38.6 against 38.8-39.6 us; the 128-way sweeps (flat, and hybrid
+// accumulating) unchanged (533.0-536.2 against 533.0-536.7 us, 542.0-542.6 against
+// 541.8-543.7 us); default-scope nt buffer stores like AdamW's measured as the global ones.
 __device__ __forceinline__ void store_whole8(float* wave_out, const float* acc) {
     const int lane = threadIdx.x & 63;
+    const auto rs = block_rsrc(wave_out, 2048);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
         const int src = 32 * h + (lane >> 1);
@@ -648,7 +656,7 @@ __device__ __forceinline__ void store_whole8(float* wave_out, const float* acc) 
             const float hi = __shfl(acc[4 + i], src, 64);
             w[i] = (lane & 1) ? hi : lo;
         }
-        st4(wave_out + 256 * h + 4 * lane, f4{w[0], w[1], w[2], w[3]});
+        bst4<kTileStoreCpol>(rs, 4 * (256 * h + 4 * lane), f4{w[0], w[1], w[2], w[3]});
     }
 }
 
@@ -1314,11 +1322,23 @@ __global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(SqTable<kCap
 
 // Stage 2: one workgroup per run sums its partials in a fixed order (lane order
 // within strided passes, then the block tree) and writes the parameter's result.
+// Each lane loads up to kSqFinalAhead of its partials before adding them (in the same
+// order), so their round trips overlap instead of following one another.
+constexpr int kSqFinalAhead = 8;
 __global__ __launch_bounds__(kSqThreads) void sqnorm_final_kernel(SqTable<kMaxSegs> t) {
     __shared__ double lds[kSqThreads / 64];
     const SqRun& r = t.run[blockIdx.x];
+    const double* p = t.partial + r.tile0;
     double acc = 0.0;
-    for (uint32_t i = threadIdx.x; i < r.ntiles; i += kSqThreads) acc = acc + t.partial[r.tile0 + i];
+    uint32_t i = threadIdx.x;
+    for (; i + (kSqFinalAhead - 1) * kSqThreads < r.ntiles; i += kSqFinalAhead * kSqThreads) {
+        double v[kSqFinalAhead];
+#pragma unroll
+        for (int u = 0; u < kSqFinalAhead; ++u) v[u] = p[i + u * kSqThreads];
+#pragma unroll
+        for (int u = 0; u < kSqFinalAhead; ++u) acc = acc + v[u];
+    }
+    for (; i < r.ntiles; i += kSqThreads) acc = acc + p[i];
     const double s = block_sum(acc, lds);
     if (threadIdx.x == 0) t.out[r.out] = s;
 }
