@@ -145,3 +145,23 @@ def test_all_cores_baseline_slices_reassemble_the_single_call_results():
         oracle.adamw(p2[a:b], g[a:b], m2[a:b], v2[a:b], step=1, **hp)
     for x, y in ((p1, p2), (m1, m2), (v1, v2)):
         assert np.array_equal(x.view(np.uint32), y.view(np.uint32))
+
+
+def test_every_committed_profile_was_taken_on_the_current_kernels():
+    """Each rocprofv3 summary under profiles/ names the sha256 of the kernel source it was taken
+    on; all of them must name the current one, so that no figure quoted from them is stale."""
+    import glob
+    import json
+    import re
+    import bench
+    cur = bench.kernel_src_hash()
+    files = sorted(glob.glob(os.path.join(ROOT, "profiles", "*")))
+    assert files
+    for path in files:
+        with open(path) as f:
+            text = f.read()
+        if path.endswith(".json"):
+            assert json.loads(text)["kernel_src_sha256"] == cur, path
+        else:
+            found = re.findall(r"kernels\.hip sha256: `([0-9a-f]{64})`", text)
+            assert found and all(h == cur for h in found), path
