@@ -11,6 +11,13 @@ Flags that matter for results:
                            no packed-fp32 instructions are generated;
   no -ffast-math / -fgpu-flush-denormals-to-zero: IEEE division, square root
                            and subnormals.
+A flag that matters for speed only:
+  -mllvm -amdgpu-kernarg-preload-count=16
+                           the first 16 dwords of a kernel's scalar arguments
+                           arrive preloaded in scalar registers (the copy engine,
+                           AdamW and the sums of squares pass what a workgroup
+                           needs first that way), so a short-lived workgroup
+                           issues its loads without waiting for a scalar load.
 """
 from __future__ import annotations
 
@@ -40,6 +47,7 @@ FLAGS = [
     "-ffp-contract=off",
     "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall",
     "-Wno-unused-command-line-argument",
     "-fvisibility=hidden",

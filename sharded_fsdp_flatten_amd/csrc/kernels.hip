@@ -57,6 +57,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <cstddef>
 #include <cstdint>
 #include <cmath>
 #include <vector>
@@ -267,7 +268,8 @@ constexpr int tile_elems() { return kThreads * Cp<SrcT, DstT>::E * Cp<SrcT, DstT
 // ---------------------------------------------------------------------------
 // segcopy
 // ---------------------------------------------------------------------------
-// One segment of a launch; the fields a single-segment launch reads come first.
+// One segment of a launch; the fields a one-block segment reads come first (the strides are
+// read only by segments of several blocks).
 struct DevSeg {
     const void* src;  // nullptr: zero fill
     void* dst;
@@ -278,6 +280,9 @@ struct DevSeg {
 // A launch's segments, passed by value in the kernel-argument block: a table of kCap entries,
 // the smallest of 1, 4, 8, 16 and kMaxSegs that holds the launch's segments, with the segments'
 // first tiles in one array next to the header and a copy of the segment with the most tiles.
+// The kernel also takes the header and that segment's one-block fields as scalar arguments
+// ahead of the table: the dispatch preloads those into scalar registers (kernel-argument
+// preloading, 16 dwords), so that segment's tiles start without a scalar load.
 template <int kCap>
 struct SegTable {
     uint32_t ntiles;
@@ -285,10 +290,10 @@ struct SegTable {
     uint32_t xcd_runs;      // tiles in XCD-chunked order (xcd_chunked)
     uint32_t hot_tiles;     // tiles of `hot`
     uint32_t start[kCap];   // seg[i].tile0; 0xFFFFFFFF past nseg
-    DevSeg hot;             // the segment with the most tiles (unused in one-segment tables)
+    DevSeg hot;             // the segment with the most tiles (the only one in one-segment tables)
     DevSeg seg[kCap];
 };
-static_assert(sizeof(SegTable<kMaxSegs>) <= 4096, "segment table must fit one kernel argument block");
+static_assert(sizeof(SegTable<kMaxSegs>) <= 4096 - 64, "segment table and scalar arguments must fit one kernel argument block");
 
 // The dispatcher deals a launch's workgroups to MI355X's eight XCDs in turn (workgroup b to
 // XCD b % 8).  This maps b to the tile it runs so that each XCD takes one contiguous run of
@@ -401,57 +406,86 @@ __device__ __forceinline__ void copy_tile(const DevSeg& sg, uint32_t local, SrcT
     const int64_t bn = (b + 1 == sg.nblk) ? sg.last_n : sg.blk_n;
     if (e0 >= bn) return;
     const int n = static_cast<int>(min(static_cast<int64_t>(kTile), bn - e0));
-    DstT* d = static_cast<DstT*>(sg.dst) + static_cast<int64_t>(b) * sg.dst_stride + e0;
+    // block offsets only for segments of several blocks: a one-block segment never reads its
+    // strides (they lie outside the preloaded part of the table)
+    int64_t doff = e0, soff = e0;
+    if (sg.nblk != 1) {
+        doff += static_cast<int64_t>(b) * sg.dst_stride;
+        soff += static_cast<int64_t>(b) * sg.src_stride;
+    }
+    DstT* d = static_cast<DstT*>(sg.dst) + doff;
     if (sg.src == nullptr) {
         tile_zero<SrcT, DstT>(d, n);
         return;
     }
-    const SrcT* s = static_cast<const SrcT*>(sg.src) + static_cast<int64_t>(b) * sg.src_stride + e0;
+    const SrcT* s = static_cast<const SrcT*>(sg.src) + soff;
     if constexpr (kGeneral)
         tile_general<SrcT, DstT>(s, d, n, lds);
     else
         tile_aligned<SrcT, DstT>(s, d, n);
 }
 
-// One tile per workgroup (grid = number of tiles).  The tile's segment comes from the table
-// through wave-uniform scalar loads, and a workgroup's first vector load waits for them, so
-// the kernel reads everything most tiles need in one round trip: the empty asm statements pin
-// the loads at the start, where the compiler would issue each just before its first use,
-// after the previous one's wait.  A one-segment table loads that segment with the header; a
-// larger one loads the copy of its segment with the most tiles and the segments' first tiles,
-// and only the tiles outside the big segment look up theirs: a count on scalar registers,
-// then one load.  GPT-175B block, rank flatten, rocprofv3 durations (cold cache, two rounds
-// on one box): one segment 18.72-18.84 us against 19.04-19.28 with a binary search of the
-// table for every tile; rank 0's five segments (four LayerNorm tensors of 12 tiles before the
-// big one) 19.20 against 20.16-20.40.  Counting instead of the binary search (a dependent load
-// per step) for the tiles outside the big segment, rocprofv3, two rounds of alternating
-// processes each: GPT-2-L block copy-out 20.34-20.52 against 21.08-21.30 us, FSDP2 rows unit
-// flatten 14.88-15.06 against 15.16-15.48 us, larger copies unchanged.  The first tiles are
-// pinned only in tables of up to 8 entries: with 16 the compiler splits the header's loads into
-// two rounds for every tile.  Five to eight segments take the 8-entry table: the GPT-2-L block's
-// rank 2 (two large segments among five) 5.62-5.76 us against 6.06-6.30 in the 16-entry table,
-// the GPT-175B step unchanged (rocprofv3, three rounds of alternating processes).
+// One tile per workgroup (grid = number of tiles).  A workgroup's first vector load waits for
+// whatever locates its tile, so the segment with the most tiles (the only one, in one-segment
+// launches) comes as scalar arguments ahead of the table, which the dispatch preloads into
+// scalar registers (kernel-argument preloading, 16 dwords): that segment's tiles issue their
+// loads without a scalar load.  Against the same fields read from the table with every load
+// pinned at the start (rocprofv3 medians, three rounds of alternating processes, each launch
+// after a 1 GiB read): GPT-175B rank flatten 18.40-18.76 against 18.70-19.24 us, its rank
+// cast 14.42-14.52 against 14.68-14.88, GPT-2-L rank flatten 5.28-5.64 against 5.64-5.98 and
+// copy-out 20.26-20.42 against 20.70-20.88 us; only the GPT-2-L rank cast measured the same or
+// slower (4.96-5.38 against 4.86-5.02 us).  Tiles outside the big segment look up theirs:
+// the segments' first tiles are loaded together (pinned by empty asm statements; the compiler
+// would otherwise issue each load just before its compare, after the previous one's wait),
+// counted on scalar registers, and the segment is loaded.  Counting instead of a binary search
+// of the table (a dependent load per step): GPT-2-L block copy-out 20.34-20.52 against
+// 21.08-21.30 us, FSDP2 rows unit flatten 14.88-15.06 against 15.16-15.48 us.  The first tiles
+// are pinned only in tables of up to 8 entries: with 16 the compiler splits their loads into two
+// rounds.  Five to eight segments take the 8-entry table: the GPT-2-L block's rank 2 (two large
+// segments among five) 5.62-5.76 us against 6.06-6.30 in the 16-entry table.
 template <typename SrcT, typename DstT, bool kGeneral, int kCap>
-__global__ __launch_bounds__(kThreads) void segcopy_kernel(SegTable<kCap> t) {
+__global__ __launch_bounds__(kThreads) void segcopy_kernel(
+    uint32_t ntiles, uint32_t xcdr, uint32_t hot_tiles, uint32_t hot_tile0, const void* hot_src,
+    void* hot_dst, int64_t hot_blk_n, int64_t hot_last_n, uint32_t hot_nblk, uint32_t hot_tpb,
+    SegTable<kCap> t) {
     constexpr int kTile = tile_elems<SrcT, DstT>();
     __shared__ __attribute__((aligned(16))) SrcT lds[kGeneral && sizeof(SrcT) == 2 ? kTile + 16 : 8];
-    const uint32_t ntiles = t.ntiles, xcdr = t.xcd_runs;
-    const DevSeg& z = kCap == 1 ? t.seg[0] : t.hot;
-    const uint32_t hot_tiles = kCap == 1 ? ntiles : t.hot_tiles;
-    asm volatile("" ::"s"(ntiles), "s"(xcdr), "s"(hot_tiles), "s"(z.src), "s"(z.dst),
-                 "s"(z.blk_n), "s"(z.last_n), "s"(z.nblk), "s"(z.tiles_per_blk), "s"(z.tile0),
-                 "s"(z.src_stride), "s"(z.dst_stride));
-    if constexpr (kCap > 1 && kCap <= 8) {
-#pragma unroll
-        for (int i = 1; i < kCap; ++i) asm volatile("" ::"s"(t.start[i]));
-    }
+    // the hot segment from the preloaded arguments; its strides (read by segments of several
+    // blocks only) from the table
+    DevSeg z;
+    z.src = hot_src;
+    z.dst = hot_dst;
+    z.blk_n = hot_blk_n;
+    z.last_n = hot_last_n;
+    z.nblk = hot_nblk;
+    z.tiles_per_blk = hot_tpb;
+    z.tile0 = hot_tile0;
+    z.unused = 0;
+    z.src_stride = t.hot.src_stride;
+    z.dst_stride = t.hot.dst_stride;
     const uint32_t tile = xcdr ? xcd_chunked<kXcdChunk>(blockIdx.x, ntiles) : blockIdx.x;
-    if (kCap == 1 || tile - z.tile0 < hot_tiles) {
-        copy_tile<SrcT, DstT, kGeneral>(z, tile - z.tile0, lds);
+    const uint32_t local = tile - hot_tile0;
+    if (kCap == 1 || local < hot_tiles) {
+        if constexpr (!kGeneral) {
+            // the common case first, in as few scalar instructions as possible: a whole tile
+            // of a one-block segment
+            const int64_t e0 = static_cast<int64_t>(local) * kTile;
+            if (hot_nblk == 1 && hot_src != nullptr && e0 + kTile <= hot_last_n) {
+                tile_aligned<SrcT, DstT>(static_cast<const SrcT*>(hot_src) + e0,
+                                         static_cast<DstT*>(hot_dst) + e0, kTile);
+                return;
+            }
+        }
+        copy_tile<SrcT, DstT, kGeneral>(z, local, lds);
         return;
     }
     // the segment holding this tile (wave-uniform): the number of later segments that start
-    // at or before it
+    // at or before it, the starts loaded together (one round trip; without the pins the
+    // compiler loads each just before its compare, after the previous one's wait)
+    if constexpr (kCap <= 8) {
+#pragma unroll
+        for (int i = 1; i < kCap; ++i) asm volatile("" ::"s"(t.start[i]));
+    }
     uint32_t k = 0;
 #pragma unroll
     for (int i = 1; i < kCap; ++i) k += t.start[i] <= tile ? 1u : 0u;
@@ -1035,7 +1069,12 @@ __device__ __forceinline__ void adam_one(const AdamArgs& a, int64_t j) {
 // One tile of kAdamThreads * 8 elements per workgroup; lane l owns vectors l and
 // l + kAdamThreads (4 elements each) of every array.
 template <bool kVec, bool kBf16>
-__global__ __launch_bounds__(kAdamThreads) void adamw_kernel(AdamArgs a) {
+// The arrays and the length are scalar arguments, so they arrive preloaded in scalar registers;
+// the per-step scalars follow as a struct (read after the loads are issued).
+__global__ __launch_bounds__(kAdamThreads) void adamw_kernel(float* p_, const float* g_, float* m_,
+                                                             float* v_, uint16_t* pb_, int64_t len,
+                                                             AdamScalars sc) {
+    const AdamArgs a{p_, g_, m_, v_, pb_, len, sc};
     constexpr int64_t kPerBlk = static_cast<int64_t>(kAdamThreads) * 8;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kPerBlk;
     if constexpr (kVec) {
@@ -1109,12 +1148,15 @@ void launch_table(const SegTable<kMaxSegs>& full, bool general, uint64_t tiles, 
         }
     }
     t.hot = full.seg[hot];
+    const DevSeg& h = t.hot;
     if (general)
         hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, true, kCap>), grid_of(tiles), dim3(kThreads), 0,
-                           stream, t);
+                           stream, t.ntiles, t.xcd_runs, t.hot_tiles, h.tile0, h.src, h.dst, h.blk_n,
+                           h.last_n, h.nblk, h.tiles_per_blk, t);
     else
         hipLaunchKernelGGL((segcopy_kernel<SrcT, DstT, false, kCap>), grid_of(tiles), dim3(kThreads), 0,
-                           stream, t);
+                           stream, t.ntiles, t.xcd_runs, t.hot_tiles, h.tile0, h.src, h.dst, h.blk_n,
+                           h.last_n, h.nblk, h.tiles_per_blk, t);
 }
 
 template <typename SrcT, typename DstT>
@@ -1248,10 +1290,10 @@ struct SqTable {
     uint32_t nrun;
     uint32_t unused;
     uint32_t start[kCap];  // run[i].tile0; 0xFFFFFFFF past nrun
-    SqRun hot;             // the run with the most tiles (unused in one-run tables)
+    SqRun hot;             // the run with the most tiles (stage 1 takes it as scalar arguments)
     SqRun run[kCap];
 };
-static_assert(sizeof(SqTable<kMaxSegs>) <= 4096, "run table must fit one kernel argument block");
+static_assert(sizeof(SqTable<kMaxSegs>) <= 4096 - 64, "run table and scalar arguments must fit one kernel argument block");
 
 // Block sum of one double per thread, in a fixed order: a shuffle tree inside each
 // wave, then the waves' sums in wave order.  Returns the sum in thread 0.
@@ -1296,28 +1338,35 @@ __device__ __forceinline__ void sq_tile(const float* g0, double* partial, const 
     if (threadIdx.x == 0) partial[tile] = s;
 }
 
-// The tile's run is found as the copy engine finds a tile's segment: the header and the run
-// with the most tiles are loaded at the start (pinned there by the empty asm statements), and
-// only tiles outside that run count the later runs that start at or before them.
+// The tile's run is found as the copy engine finds a tile's segment: the run with the most
+// tiles comes as scalar arguments ahead of the table (preloaded in scalar registers), and only
+// tiles outside that run load the runs' first tiles (together, pinned by the empty asm
+// statements) and count those that start at or before them.
 template <int kCap>
-__global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(SqTable<kCap> t) {
+__global__ __launch_bounds__(kSqThreads) void sqnorm_partial_kernel(
+    const float* g, double* partial, int64_t hot_offset, int64_t hot_n, uint32_t hot_tile0,
+    uint32_t hot_ntiles, SqTable<kCap> t) {
     __shared__ double lds[kSqThreads / 64];
     const uint32_t tile = blockIdx.x;
-    const SqRun& z = kCap == 1 ? t.run[0] : t.hot;
-    asm volatile("" ::"s"(t.g), "s"(t.partial), "s"(z.offset), "s"(z.n), "s"(z.tile0),
-                 "s"(z.ntiles));
-    if constexpr (kCap > 1 && kCap <= 8) {
+    if (kCap == 1 || tile - hot_tile0 < hot_ntiles) {
+        SqRun z;
+        z.offset = hot_offset;
+        z.n = hot_n;
+        z.tile0 = hot_tile0;
+        z.ntiles = hot_ntiles;
+        z.out = 0;
+        z.unused = 0;
+        sq_tile(g, partial, z, tile, lds);
+        return;
+    }
+    if constexpr (kCap <= 8) {
 #pragma unroll
         for (int i = 1; i < kCap; ++i) asm volatile("" ::"s"(t.start[i]));
-    }
-    if (kCap == 1 || tile - z.tile0 < z.ntiles) {
-        sq_tile(t.g, t.partial, z, tile, lds);
-        return;
     }
     uint32_t k = 0;
 #pragma unroll
     for (int i = 1; i < kCap; ++i) k += t.start[i] <= tile ? 1u : 0u;
-    sq_tile(t.g, t.partial, t.run[k], tile, lds);
+    sq_tile(g, partial, t.run[k], tile, lds);
 }
 
 // Stage 2: one workgroup per run sums its partials in a fixed order (lane order
@@ -1549,7 +1598,6 @@ hipError_t launch_grad_accumulate(const uint16_t* grad, float* acc, int64_t len,
 hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* pb, int64_t len,
                         const AdamScalars& s, hipStream_t stream) {
     if (len <= 0) return hipSuccess;
-    AdamArgs a{p, g, m, v, pb, len, s};
     const bool vec = aligned_to(p, 16) && aligned_to(g, 16) && aligned_to(m, 16) &&
                      aligned_to(v, 16) && (pb == nullptr || aligned_to(pb, 8));
     const int64_t per_blk = static_cast<int64_t>(kAdamThreads) * 8;
@@ -1558,13 +1606,13 @@ hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* 
     if (vec) {
         if (pb)
             hipLaunchKernelGGL((adamw_kernel<true, true>), grid_of(blocks), dim3(kAdamThreads), 0,
-                               stream, a);
+                               stream, p, g, m, v, pb, len, s);
         else
             hipLaunchKernelGGL((adamw_kernel<true, false>), grid_of(blocks), dim3(kAdamThreads),
-                               0, stream, a);
+                               0, stream, p, g, m, v, pb, len, s);
     } else {
         hipLaunchKernelGGL((adamw_kernel<false, false>), grid_of(blocks), dim3(kAdamThreads), 0,
-                           stream, a);
+                           stream, p, g, m, v, pb, len, s);
     }
     return hipGetLastError();
 }
@@ -1631,7 +1679,9 @@ void launch_sq_partial(const SqTable<kMaxSegs>& busy, uint32_t tiles, hipStream_
         if (busy.run[i].ntiles > busy.run[hot].ntiles) hot = i;
     }
     t.hot = busy.run[hot];
-    hipLaunchKernelGGL((sqnorm_partial_kernel<kCap>), grid_of(tiles), dim3(kSqThreads), 0, stream, t);
+    const SqRun& h = t.hot;
+    hipLaunchKernelGGL((sqnorm_partial_kernel<kCap>), grid_of(tiles), dim3(kSqThreads), 0, stream,
+                       t.g, t.partial, h.offset, h.n, h.tile0, h.ntiles, t);
 }
 
 }  // namespace
