@@ -119,7 +119,15 @@ constexpr int kSweepV = 16;
 constexpr int kGroupSweepV = 8;
 constexpr int kGroupSweepLongAhead = 2;
 constexpr int64_t kGroupSweepMinRunTiles = 12288;
-constexpr int kUnscaleVpl = 4;       // 4-element vectors per lane in the gradient unscale
+// 4-element vectors per lane in the gradient unscale: four from kUnscaleLongLen elements on, two
+// below, where four leave too few workgroups for the device (rocprofv3 medians, three rounds of
+// alternating processes, each launch after a 1 GiB read): GPT-175B shard (14.2 M) 19.36-19.46 us
+// with four against 19.82-19.86 with two and 19.38-20.06 with one; T5 shard (25.2 M) 30.50-30.64
+// against 30.40-30.46 and 31.82-32.14; GPT-2-L shard (2.5 M) 7.82-7.90 against 6.10-6.14 and
+// 6.12-6.24 us.
+constexpr int kUnscaleVpl = 4;
+constexpr int kUnscaleShortVpl = 2;
+constexpr int64_t kUnscaleLongLen = int64_t{1} << 23;
 // The in-place local accumulation over all L of the GPT-175B unit (885k blocks of 2048) takes
 // runs of 128 blocks per XCD: 6.38-6.40 TB/s, against 5.87-5.88 in dispatch order and runs of
 // 16 / 32 / 64 / 256 blocks 5.98-5.99 / 6.12-6.21 / 6.32-6.34 / 6.37-6.38 (HIP events, two
@@ -1228,10 +1236,9 @@ void launch_reduce_mode(const ReduceArgs& a, bool hybrid, bool accum, dim3 grid,
 // In place: plain loads and nt stores (as AdamW).  A wave that saw a non-finite
 // input has one lane store 1.0f into the flag (vector store; every writer stores
 // the same value, so concurrent stores agree).  found == nullptr: scaling only.
-template <bool kVec>
+template <bool kVec, int kV>
 __global__ __launch_bounds__(kThreads) void unscale_kernel(float* __restrict__ g, int64_t len,
                                                            float inv, float* __restrict__ found) {
-    constexpr int kV = kUnscaleVpl;
     constexpr int64_t kPerBlk = static_cast<int64_t>(kThreads) * 4 * kV;
     const int64_t base = static_cast<int64_t>(blockIdx.x) * kPerBlk;
     bool bad = false;
@@ -1620,14 +1627,23 @@ hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* 
 hipError_t launch_grad_unscale(float* g, int64_t len, float inv_scale, float* found_inf,
                                hipStream_t stream) {
     if (len <= 0) return hipSuccess;
-    const int64_t per_blk = static_cast<int64_t>(kThreads) * 4 * kUnscaleVpl;
+    const bool longer = len >= kUnscaleLongLen;
+    const int64_t per_blk = static_cast<int64_t>(kThreads) * 4 * (longer ? kUnscaleVpl : kUnscaleShortVpl);
     const int64_t blocks = (len + per_blk - 1) / per_blk;
     if (blocks > 0x7FFFFFFFll) return hipErrorInvalidValue;
     const dim3 grid = grid_of(blocks), block(kThreads);
-    if (aligned_to(g, 16))
-        hipLaunchKernelGGL((unscale_kernel<true>), grid, block, 0, stream, g, len, inv_scale, found_inf);
-    else
-        hipLaunchKernelGGL((unscale_kernel<false>), grid, block, 0, stream, g, len, inv_scale, found_inf);
+    const bool vec = aligned_to(g, 16);
+    if (longer) {
+        if (vec)
+            hipLaunchKernelGGL((unscale_kernel<true, kUnscaleVpl>), grid, block, 0, stream, g, len, inv_scale, found_inf);
+        else
+            hipLaunchKernelGGL((unscale_kernel<false, kUnscaleVpl>), grid, block, 0, stream, g, len, inv_scale, found_inf);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((unscale_kernel<true, kUnscaleShortVpl>), grid, block, 0, stream, g, len, inv_scale, found_inf);
+        else
+            hipLaunchKernelGGL((unscale_kernel<false, kUnscaleShortVpl>), grid, block, 0, stream, g, len, inv_scale, found_inf);
+    }
     return hipGetLastError();
 }
 
